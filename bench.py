@@ -1,0 +1,277 @@
+"""Benchmark of the W8A8 linear hot path on one MI355X.
+
+A step is one pass of the int W8A8 linear forward on the headline shape
+(X bf16 [4096, 3072], W [12288, 3072] int8 tensor-wise, bias [12288]):
+row-wise act-quant of X, then the int8 GEMM with the fused dequant epilogue
+writing bf16 Y.  Weight quantization is done once per weight before timing
+(frozen weights).  Inputs live in HBM before the timed region; R buffer sets
+(X, Xq, sx, Wq, Y) are rotated so that every step reads cold HBM rather than
+the 256 MB Infinity Cache.
+
+Printed: one JSON line with the step throughput (TOPS over the whole step),
+the GEMM kernel's roofline (int8 MFMA dense peak 5.0 POPS), the act-quant
+kernel's HBM rate, per-row figures of the other paths (fp8 train step, DiT
+shapes, SVDQuant, Q8_0) and the CPU oracle timed on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POPS
+PEAK_FP8_TFLOPS = 5000.0    # dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0       # HBM3E 8 TB/s
+M, K, N = 4096, 3072, 12288
+ROTATE = 4
+
+
+def _args():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-rows", action="store_true", help="skip the per-row figures of the other paths")
+    p.add_argument("--cpu-rows", type=int, default=96, help="rows of the oracle sample")
+    return p.parse_args()
+
+
+def _bf16(t_bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(t_bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _time_launches(fn, iters, warmup):
+    """Average duration (ms) of fn(i) over iters launches, HIP events on the
+    current stream (the stream the library launches on)."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(iters):
+        fn(i)
+    e1.record()
+    e1.synchronize()
+    return e0.elapsed_time(e1) / iters
+
+
+def _kernel_hash():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.hpp", "internal.hpp"):
+        with open(os.path.join(ROOT, "w8a8_quantized_linear_quant_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic_from_profile(kernel_hash):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "gemm_int8_M4096_N12288_K3072_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_hash") != kernel_hash:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(x_bits, w_bits, b_bits, rows):
+    """The oracle (plain C, one thread) on the first `rows` rows of the same
+    workload: act-quant + weight quant + linear, scaled to TOPS of the linear."""
+    import oracle
+    xs = x_bits[:rows]
+    t0 = time.perf_counter()
+    wq, _, sw = oracle.quant_weight_tensorwise(oracle.INT8, w_bits)
+    t1 = time.perf_counter()
+    xq, sx = oracle.quant_act_rowwise(oracle.INT8, xs)
+    oracle.linear(oracle.INT8, xq, sx, wq, sw, b_bits)
+    t2 = time.perf_counter()
+    ops = 2.0 * rows * N * K
+    return {"value": round(ops / (t2 - t1) / 1e12, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
+            "sample": f"first {rows} of {M} rows: act-quant + int8 linear ({rows}x{N}x{K}); "
+                      f"weight quant ({N}x{K}) timed apart: {t1 - t0:.2f} s",
+            "seconds": round(t2 - t1, 2)}
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path is single-GPU "
+              "and multi-GPU sharding is a design note, not a measured configuration.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import workloads
+    import w8a8_quantized_linear_quant_amd as w8
+
+    torch.cuda.init()
+    d = workloads.svdq()
+    x_bits, r_bits, b_bits = d["x"], d["r"], d["bias"]
+    print(f"[bench] inputs ready: X {x_bits.shape}, W {r_bits.shape}", file=sys.stderr, flush=True)
+
+    # R rotating buffer sets; the weight is quantized once per set (amortized).
+    sets = []
+    x0, w0, bias = _bf16(x_bits), _bf16(r_bits), _bf16(b_bits)
+    for i in range(ROTATE):
+        xi = x0 if i == 0 else x0.clone()
+        wq, _, sw = w8.w8a8_quant_weight_tensorwise(w0 if i == 0 else w0.clone())
+        sets.append({
+            "x": xi, "wq": wq, "sw": sw, "bias": bias.clone(),
+            "xq": torch.empty((M, K), dtype=torch.int8, device="cuda"),
+            "sx": torch.empty(M, dtype=torch.float32, device="cuda"),
+            "y": torch.empty((M, N), dtype=torch.bfloat16, device="cuda"),
+        })
+    torch.cuda.synchronize()
+
+    def act_quant(i):
+        s = sets[i % ROTATE]
+        w8.w8a8_quant_act_rowwise(s["x"], out=s["xq"], scale=s["sx"])
+
+    def gemm(i):
+        s = sets[i % ROTATE]
+        w8.w8a8_linear(s["xq"], s["sx"], s["wq"], s["sw"], s["bias"], out=s["y"])
+
+    def step(i):
+        act_quant(i)
+        gemm(i)
+
+    # ---- the timed steps
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall0 = time.perf_counter()
+    e0.record()
+    for i in range(args.steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    ops = 2.0 * M * N * K
+    tops = ops / (ms_step * 1e-3) / 1e12
+    print(f"[bench] step {ms_step * 1e3:.1f} us ({t_wall:.2f} s wall for {args.steps} steps)", file=sys.stderr,
+          flush=True)
+
+    # ---- per-kernel averages (same launches, timed apart)
+    iters = max(args.steps, 20)
+    ms_gemm = _time_launches(gemm, iters, 5)
+    ms_aq = _time_launches(act_quant, iters, 5)
+    gemm_tops = ops / (ms_gemm * 1e-3) / 1e12
+    aq_bytes = 2.0 * M * K + M * K + 4.0 * M
+    aq_gbs = aq_bytes / (ms_aq * 1e-3) / 1e9
+    khash = _kernel_hash()
+    roofline = {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
+                "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": _traffic_from_profile(khash),
+                "kernel": "gemm_kernel<int8, bf16 epilogue>", "us_per_launch": round(ms_gemm * 1e3, 2),
+                "algorithmic_ops_per_launch": ops, "kernel_source_hash": khash}
+    act = {"bound": "hbm", "achieved": round(aq_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+           "frac": round(aq_gbs / PEAK_HBM_GBS, 4), "us_per_launch": round(ms_aq * 1e3, 2),
+           "algorithmic_bytes_per_launch": aq_bytes, "kernel": "act_quant_rowwise_kernel<int8>"}
+
+    rows = {} if args.no_rows else other_rows(w8, torch, workloads, args)
+    for s in sets:
+        s.clear()
+    torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(x_bits, r_bits, b_bits, args.cpu_rows)
+
+    out = {
+        "metric": "W8A8 linear TOPS (M4096 K3072 N12288) + act-quant GB/s, % of roofline",
+        "value": round(tops, 1), "unit": "TOPS", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int8", "data": "synthetic (seeded numpy PCG64, transformer-shaped; no dataset)",
+        "config": {"workload": "int W8A8 linear forward: row-wise act-quant X[4096,3072] bf16 + int8 GEMM "
+                               "vs W[12288,3072] (tensor-wise) + dequant/bias epilogue -> bf16 Y",
+                   "M": M, "K": K, "N": N, "bias": True, "rotating_buffer_sets": ROTATE},
+        "roofline": roofline,
+        "act_quant": act,
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def other_rows(w8, torch, workloads, args):
+    """Per-kernel figures of the other hot-path rows (not part of `value`)."""
+    res = {}
+    iters = 20
+    # SVDQuant at the headline shape, r = 32
+    d = workloads.svdq()
+    x, l1, l2, rr, b = (_bf16(d[k]) for k in ("x", "l1", "l2", "r", "bias"))
+    rq, _, sr = w8.w8a8_quant_weight_tensorwise(rr)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    sx = torch.empty(M, dtype=torch.float32, device="cuda")
+    ws = torch.empty(w8.svdq_workspace_bytes(M, 32), dtype=torch.uint8, device="cuda")
+    ms = _time_launches(lambda i: w8.svdq_linear(x, rq, sr, l1, l2, b, out=y, xq_out=xq, x_scale_out=sx,
+                                                 workspace=ws), iters, 3)
+    ops = 2.0 * M * N * K + 2.0 * M * K * 32 + 2.0 * M * 32 * N
+    res["svdq_linear_M4096_K3072_N12288_r32"] = {"us": round(ms * 1e3, 1), "TOPS": round(ops / ms / 1e9, 1)}
+    del x, l1, l2, rr, b, rq, y, xq, ws
+    # DiT shapes
+    d = workloads.dit()
+    x = _bf16(d["x"])
+    xq, sx = w8.w8a8_quant_act_rowwise(x)
+    for name, wk, bk in (("dit_M4608_K3072_N3072", "w1", "b1"), ("dit_M4608_K3072_N12288", "w2", "b2")):
+        wq, _, sw = w8.w8a8_quant_weight_tensorwise(_bf16(d[wk]))
+        bb = _bf16(d[bk])
+        nn = wq.shape[0]
+        y = torch.empty((4608, nn), dtype=torch.bfloat16, device="cuda")
+        ms = _time_launches(lambda i: w8.w8a8_linear(xq, sx, wq, sw, bb, out=y), iters, 3)
+        res[name] = {"us": round(ms * 1e3, 1), "TOPS": round(2.0 * 4608 * nn * 3072 / ms / 1e9, 1)}
+    del x, xq, y
+    # fp8 train step shapes
+    d = workloads.fp8_step()
+    wq, wqt, sw = w8.w8a8_quant_weight_tensorwise(_bf16(d["w"]), qtype=w8.FP8_E4M3, transposed=True)
+    x = _bf16(d["x"])
+    xq, sx = w8.w8a8_quant_act_rowwise(x, qtype=w8.FP8_E4M3)
+    y = torch.empty((8192, N), dtype=torch.bfloat16, device="cuda")
+    ms = _time_launches(lambda i: w8.w8a8_linear(xq, sx, wq, sw, out=y), iters, 3)
+    res["fp8_fwd_M8192_K3072_N12288"] = {"us": round(ms * 1e3, 1),
+                                         "TFLOPS": round(2.0 * 8192 * N * K / ms / 1e9, 1)}
+    dy = _bf16(d["dy"])
+    dyq = torch.empty((8192, N), dtype=torch.float8_e4m3fn, device="cuda")
+    sdy = torch.empty(8192, dtype=torch.float32, device="cuda")
+    ms = _time_launches(lambda i: w8.w8a8_quant_act_rowwise(dy, qtype=w8.FP8_E4M3, out=dyq, scale=sdy), iters, 3)
+    bytes_ = 3.0 * 8192 * N + 4 * 8192
+    res["act_quant_fp8_dY_8192x12288"] = {"us": round(ms * 1e3, 1), "GB/s": round(bytes_ / ms / 1e6, 1)}
+    dx = torch.empty((8192, K), dtype=torch.bfloat16, device="cuda")
+    ms = _time_launches(lambda i: w8.w8a8_linear_backward_dx(dyq, sdy, wqt, sw, out=dx), iters, 3)
+    res["fp8_bwd_dx_M8192_N12288_K3072"] = {"us": round(ms * 1e3, 1),
+                                            "TFLOPS": round(2.0 * 8192 * N * K / ms / 1e9, 1)}
+    del wq, wqt, x, xq, y, dy, dyq, dx
+    # Q8_0
+    v = torch.from_numpy(workloads.q8_0_vector()).cuda()
+    n = v.numel()
+    blob = torch.empty(w8.q8_0_nbytes(n), dtype=torch.uint8, device="cuda")
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    ms = _time_launches(lambda i: w8.q8_0_quantize(v, out=blob), iters, 3)
+    qbytes = 4.0 * n + w8.q8_0_nbytes(n)
+    res["q8_0_quantize_n16777221"] = {"us": round(ms * 1e3, 1), "GB/s": round(qbytes / ms / 1e6, 1)}
+    ms = _time_launches(lambda i: w8.q8_0_dequantize(blob, n, out=out), iters, 3)
+    res["q8_0_dequantize_n16777221"] = {"us": round(ms * 1e3, 1), "GB/s": round(qbytes / ms / 1e6, 1)}
+    torch.cuda.synchronize()
+    return res
+
+
+if __name__ == "__main__":
+    main()

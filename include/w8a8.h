@@ -1,0 +1,207 @@
+/*
+ * w8a8.h -- C ABI of the MI355X (gfx950) W8A8 quantized-linear library.
+ *
+ * What it computes (the pages this follows):
+ *  - OneTrainer wiki "Quantization", "Technical" entries of the int W8A8 and
+ *    float W8A8 types: weights quantized tensor-wise to int8 or float8 e4m3,
+ *    activations quantized token-wise (one scale per row) during training,
+ *    and the linear layer's matrix product done in 8 bits.
+ *  - bitsandbytes #1401 "LLM.int8() Refactoring: Part 1", "Enhancements": one
+ *    fused kernel calibrates the row scale and quantizes; row-major data only,
+ *    no layout transforms; calls usable under graph capture.
+ *  - OneTrainer PR #1034, "SVDQuant" (and the wiki's SVDQuant entry): a bf16
+ *    low-rank branch added to the quantized product of the residual weight.
+ *  - entrenar 0.7.8 src/quant/gguf_quant/q8_0.rs: GGUF Q8_0 blocks (32 values,
+ *    f16 scale, 34 bytes), Q8_0::quantize and Q8_0::dequantize.
+ *
+ * Shared rules
+ *  - Absmax scale of a group (a row, a whole tensor, a 32-value block):
+ *    s = 1e-10f if absmax < 1e-10f, else absmax / QMAX in f32 (QMAX = 127 for
+ *    int8, 448 for e4m3).  int8 code = clamp(round_half_even(f32(x / s)),
+ *    -128, 127); e4m3 code = e4m3_rne(clamp(f32(x / s), -448, 448)).
+ *  - fp8 is OCP FP8 E4M3FN (bias 7, max finite 448, no infinities).
+ *  - bf16 and f16 values travel as uint16_t bit patterns; codes as bytes.
+ *  - Row-major only.  X is [M, K] (tokens x in-features), W is [N, K] (the
+ *    nn.Linear [out, in] layout), Y is [M, N].
+ *  - Inputs are finite (NaN/Inf in inputs give unspecified codes).
+ *
+ * Ownership and execution
+ *  - Every tensor argument is a DEVICE pointer owned by the caller, including
+ *    workspaces.  The library never allocates, frees, synchronizes or reads
+ *    device memory from the host; it validates arguments on the host,
+ *    enqueues kernels on `stream` (NULL = the default stream) and returns.
+ *    Calls can therefore be captured into a HIP graph.  No global mutable
+ *    state; calls on different streams with disjoint outputs may run
+ *    concurrently.
+ *  - All pointers must be 16-byte aligned (misaligned buffers were a known
+ *    failure mode of the prior art: "offloading alignment 16").
+ *
+ * Errors
+ *  - Arguments are checked before anything is launched; on an error nothing
+ *    is launched and one of the codes below is returned.  Sizes of 0 are a
+ *    successful no-op.  A launch failure reported by hipGetLastError()
+ *    returns W8A8_ERR_HIP.  No C++ exception crosses this interface.
+ */
+#ifndef W8A8_H_
+#define W8A8_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W8A8_OK = 0,
+    W8A8_ERR_INVALID_ARG = 1, /* null required pointer, negative size, bad enum, r outside [1, 64] */
+    W8A8_ERR_SHAPE = 2,       /* a size or stride that the layout rules below forbid */
+    W8A8_ERR_ALIGN = 3,       /* a pointer that is not 16-byte aligned */
+    W8A8_ERR_UNSUPPORTED = 4, /* a combination this build does not implement */
+    W8A8_ERR_HIP = 5          /* the HIP runtime reported a launch error */
+} w8a8_status;
+
+typedef enum {
+    W8A8_INT8 = 0,     /* int8 codes, int32 accumulation */
+    W8A8_FP8_E4M3 = 1  /* OCP e4m3 codes, f32 accumulation */
+} w8a8_qtype;
+
+/* Human-readable name of a status code (static string). */
+const char *w8a8_status_str(w8a8_status status);
+
+/* ------------------------------------------------------------------ weights */
+
+/* Bytes of device workspace w8a8_quant_weight_tensorwise needs for W [N, K]. */
+size_t w8a8_weight_workspace_bytes(int64_t N, int64_t K);
+
+/*
+ * Tensor-wise weight quantization (wiki "Quantization": int W8A8 / float W8A8
+ * "Tensor-wise quantization of weights").  One scale for all of W:
+ *   w_scale[0] = absmax scale of W;  wq[n, k] = code(W[n, k], w_scale).
+ *   w      bf16 [N, K], contiguous.
+ *   wq     codes [N, K], contiguous (int8 or e4m3 bytes).
+ *   wq_t   optional (NULL to skip): the same codes transposed, [K, N]
+ *          contiguous -- the operand layout the input-gradient product
+ *          dX = dY . W needs (see w8a8_linear_backward_dx).  Requires N % 16 == 0.
+ *   w_scale one f32 (device).
+ *   workspace  w8a8_weight_workspace_bytes(N, K) bytes of device scratch
+ *          (partial maxima; no clearing needed).
+ * Two kernels: per-block partial maxima, then a kernel that re-reduces them
+ * (deterministic, no atomics) and writes the codes.
+ * Shape rules: N, K >= 0; K % 8 == 0.
+ */
+w8a8_status w8a8_quant_weight_tensorwise(w8a8_qtype qtype, const uint16_t *w, int64_t N, int64_t K,
+                                         void *wq, void *wq_t, float *w_scale, void *workspace,
+                                         hipStream_t stream);
+
+/* -------------------------------------------------------------- activations */
+
+/*
+ * Row-wise (token-wise) activation quantization -- bitsandbytes' fused
+ * "activation scale calibration and quantization" kernel (#1401, Enhancements)
+ * applied to the W8A8 types of the OneTrainer wiki.  One pass over X:
+ *   x_scale[m] = absmax scale of row m;  xq[m, k] = code(X[m, k], x_scale[m]).
+ *   x      bf16 [M, ldx]; the first K columns of each row are used.  The
+ *          buffer spans M * ldx elements.
+ *   xq     codes [M, ldq]; columns K .. ldq-1 are written as zero, so a
+ *          caller can pad K up to the 16-multiple the GEMM needs.
+ *   x_scale f32 [M].
+ * Shape rules: M, K >= 0; ldx >= K, ldx % 8 == 0; ldq >= K, ldq % 16 == 0.
+ */
+w8a8_status w8a8_quant_act_rowwise(w8a8_qtype qtype, const uint16_t *x, int64_t M, int64_t K,
+                                   int64_t ldx, void *xq, int64_t ldq, float *x_scale,
+                                   hipStream_t stream);
+
+/* --------------------------------------------------------------- the linear */
+
+/*
+ * W8A8 linear (wiki "Quantization": "Linear layer matrix multiplications are
+ * performed in int8" / "in float8") with the dequantization fused into the
+ * product's epilogue:
+ *   acc[m, n] = sum_k xq[m, k] * wq[n, k]   (int32 exact, or f32 for e4m3)
+ *   y[m, n]   = bf16(acc[m, n] * x_scale[m] * w_scale[0] + bias[n])
+ *   xq [M, K] codes, x_scale f32 [M]; wq [N, K] codes, w_scale one f32;
+ *   bias bf16 [N] or NULL; y bf16 [M, N].
+ * Shape rules: M, N >= 0; K >= 16, K % 16 == 0 (pad K with zero codes: a zero
+ * code adds exactly 0).  Any M and N, including ragged tile tails.
+ */
+w8a8_status w8a8_linear(w8a8_qtype qtype, const void *xq, const float *x_scale, const void *wq,
+                        const float *w_scale, const uint16_t *bias, int64_t M, int64_t N, int64_t K,
+                        uint16_t *y, hipStream_t stream);
+
+/*
+ * Input gradient of the W8A8 linear with frozen W ("Activations are quantized
+ * token-wise during training"): dX = dY . W, from dY quantized row-wise
+ * (dyq [M, N], dy_scale f32 [M]) and the transposed weight codes produced by
+ * w8a8_quant_weight_tensorwise (wq_t [K, N], w_scale):
+ *   dx[m, k] = bf16(sum_n dyq[m, n] * wq_t[k, n] * dy_scale[m] * w_scale[0]).
+ * The same product kernel as w8a8_linear with the roles (K <- N, N <- K).
+ * Shape rules: M, K >= 0; N >= 16, N % 16 == 0.
+ */
+w8a8_status w8a8_linear_backward_dx(w8a8_qtype qtype, const void *dyq, const float *dy_scale,
+                                    const void *wq_t, const float *w_scale, int64_t M, int64_t N,
+                                    int64_t K, uint16_t *dx, hipStream_t stream);
+
+/*
+ * Raw int32 accumulators of the int8 product (a test and debugging export):
+ *   acc[m, n] = sum_k xq[m, k] * wq[n, k], exact (caller keeps |acc| < 2^31).
+ * Same kernel and shape rules as w8a8_linear with W8A8_INT8.
+ */
+w8a8_status w8a8_gemm_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64_t K,
+                          int32_t *acc, hipStream_t stream);
+
+/* ------------------------------------------------------------------ SVDQuant */
+
+/* Bytes of device workspace svdq_linear needs: U, f32 [M, r] (two bf16
+ * halves of it, hi and lo, [M, r] each). */
+size_t svdq_workspace_bytes(int64_t M, int64_t r);
+
+/*
+ * SVDQuant-style linear (OneTrainer PR #1034 "SVDQuant"; wiki: SVDQuant with
+ * bf16 factors, rank 16-32): W ~ L2 . L1 + R with the residual R quantized
+ * tensor-wise and a bf16 low-rank pair kept unquantized:
+ *   x_scale_out, xq_out = row-wise quantization of X (as w8a8_quant_act_rowwise)
+ *   u[m, j]  = sum_k X[m, k] * L1[j, k]          (f32, unrounded to bf16)
+ *   y[m, n]  = bf16(acc[m, n] * x_scale[m] * r_scale[0]
+ *                   + sum_j u[m, j] * L2[n, j] + bias[n])
+ *   x  bf16 [M, K]; rq codes [N, K], r_scale one f32; l1 bf16 [r, K] (down-
+ *   projection, nn.Linear layout); l2 bf16 [N, r] (up-projection); bias bf16
+ *   [N] or NULL; y bf16 [M, N]; xq_out codes [M, K]; x_scale_out f32 [M];
+ *   workspace svdq_workspace_bytes(M, r) bytes.
+ * Two launches: act-quant fused with the down-projection, then the 8-bit
+ * product whose epilogue adds the up-projection (bf16 MFMA on a hi/lo bf16
+ * split of u, so u keeps ~16 bits of precision).
+ * Shape rules: as w8a8_linear; r in {16, 32, 48, 64}.
+ */
+w8a8_status svdq_linear(w8a8_qtype qtype, const uint16_t *x, int64_t M, int64_t K, const void *rq,
+                        const float *r_scale, const uint16_t *l1, const uint16_t *l2, int64_t r,
+                        const uint16_t *bias, int64_t N, uint16_t *y, void *xq_out,
+                        float *x_scale_out, void *workspace, hipStream_t stream);
+
+/* -------------------------------------------------------------------- Q8_0 */
+
+/* Size in bytes of n values in GGUF Q8_0 blocks: 34 * ceil(n / 32) (struct
+ * Q8_0: "32 values -> 34 bytes (2 scale + 32 data)").  Returns 0 for n < 0. */
+size_t q8_0_nbytes(int64_t n);
+
+/*
+ * Q8_0::quantize: for each block of 32 values (the last one may be partial),
+ * s = absmax scale of the block's real values (int8 rule above), codes from
+ * the f32 s, the block written as {f16 d = f16_rne(s), int8 qs[32]} in 34
+ * bytes (d little-endian first); pad codes of a partial last block are 0.
+ *   x f32 [n]; blocks q8_0_nbytes(n) bytes.
+ */
+w8a8_status q8_0_quantize(const float *x, int64_t n, void *blocks, hipStream_t stream);
+
+/*
+ * Q8_0::dequantize with the stored f16 scale: y[i] = f32(qs[i]) * f32(d) of
+ * block i / 32 (an exact product).  blocks q8_0_nbytes(n) bytes; y f32 [n].
+ */
+w8a8_status q8_0_dequantize(const void *blocks, int64_t n, float *y, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W8A8_H_ */

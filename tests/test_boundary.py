@@ -1,0 +1,107 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments before launching anything.  Only
+error paths and zero-size no-ops are called (they touch no device memory)."""
+import ctypes
+
+import pytest
+
+import w8a8_quantized_linear_quant_amd as w8
+
+lib = w8.library()
+OK, INVALID, SHAPE, ALIGN, UNSUPPORTED, HIPERR = range(6)
+A = 1 << 20       # a 16-byte aligned fake address (never dereferenced)
+MIS = A + 1       # misaligned by one byte
+NULL = None
+
+
+def test_exports_match_header():
+    names = w8.exported_names_in_header()
+    assert len(names) == 12
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code in range(6):
+        assert lib.w8a8_status_str(code).decode().startswith("W8A8_")
+    assert b"unknown" in lib.w8a8_status_str(99)
+
+
+def test_sizes():
+    assert lib.q8_0_nbytes(16_777_221) == 17_825_826
+    assert lib.q8_0_nbytes(0) == 0 and lib.q8_0_nbytes(-1) == 0
+    assert [lib.q8_0_nbytes(n) for n in (1, 31, 32, 33, 64, 65)] == [34, 34, 34, 68, 68, 102]
+    assert lib.svdq_workspace_bytes(4096, 32) == 2 * 4096 * 32 * 2
+    assert lib.svdq_workspace_bytes(10, 5) == 2 * 10 * 16 * 2
+    assert lib.svdq_workspace_bytes(10, 0) == 0 and lib.svdq_workspace_bytes(10, 65) == 0
+    assert lib.w8a8_weight_workspace_bytes(12288, 3072) > 0
+
+
+def test_act_quant_rejects():
+    f = lib.w8a8_quant_act_rowwise
+    assert f(2, A, 4, 64, 64, A, 64, A, NULL) == INVALID           # bad qtype
+    assert f(0, A, -1, 64, 64, A, 64, A, NULL) == INVALID          # negative M
+    assert f(0, NULL, 4, 64, 64, A, 64, A, NULL) == INVALID        # null x
+    assert f(0, A, 4, 64, 60, A, 64, A, NULL) == SHAPE             # ldx < K
+    assert f(0, A, 4, 64, 68, A, 64, A, NULL) == SHAPE             # ldx % 8
+    assert f(0, A, 4, 64, 64, A, 72, A, NULL) == SHAPE             # ldq % 16
+    assert f(0, MIS, 4, 64, 64, A, 64, A, NULL) == ALIGN
+    assert f(1, A, 4, 64, 64, A, 64, MIS, NULL) == ALIGN
+    assert f(0, NULL, 0, 64, 64, NULL, 64, NULL, NULL) == OK       # M = 0: no-op
+
+
+def test_linear_rejects():
+    f = lib.w8a8_linear
+    assert f(0, A, A, A, A, NULL, 64, 64, 40, A, NULL) == SHAPE    # K % 16
+    assert f(0, A, A, A, A, NULL, 64, 64, 0, A, NULL) == SHAPE     # K = 0
+    assert f(0, A, A, A, A, NULL, -1, 64, 64, A, NULL) == INVALID
+    assert f(0, NULL, A, A, A, NULL, 64, 64, 64, A, NULL) == INVALID
+    assert f(0, A, NULL, A, A, NULL, 64, 64, 64, A, NULL) == INVALID
+    assert f(0, MIS, A, A, A, NULL, 64, 64, 64, A, NULL) == ALIGN
+    assert f(0, A, A, A, A, MIS, 64, 64, 64, A, NULL) == ALIGN     # misaligned bias
+    assert f(7, A, A, A, A, NULL, 64, 64, 64, A, NULL) == INVALID
+    assert f(0, A, A, A, A, NULL, 0, 64, 64, A, NULL) == OK        # M = 0: no-op
+    assert f(1, A, A, A, A, NULL, 64, 0, 64, A, NULL) == OK        # N = 0: no-op
+    g = lib.w8a8_gemm_i32
+    assert g(A, A, 8, 8, 24, A, NULL) == SHAPE
+    assert g(A, A, 8, 8, 32, MIS, NULL) == ALIGN
+    b = lib.w8a8_linear_backward_dx
+    assert b(1, A, A, A, A, 8, 24, 32, A, NULL) == SHAPE           # reduction N % 16
+
+
+def test_weight_quant_rejects():
+    f = lib.w8a8_quant_weight_tensorwise
+    assert f(0, A, 64, 60, A, NULL, A, A, NULL) == SHAPE           # K % 8
+    assert f(0, A, 24, 64, A, A, A, A, NULL) == SHAPE              # transposed copy needs N % 16
+    assert f(0, A, 64, 64, A, NULL, A, NULL, NULL) == INVALID      # no workspace
+    assert f(0, A, 64, 64, MIS, NULL, A, A, NULL) == ALIGN
+    assert f(3, A, 64, 64, A, NULL, A, A, NULL) == INVALID
+
+
+def test_svdq_rejects():
+    f = lib.svdq_linear
+    args = lambda **kw: [kw.get("qt", 0), A, kw.get("M", 64), kw.get("K", 64), A, A, A, A, kw.get("r", 16),
+                         NULL, kw.get("N", 64), A, A, A, kw.get("ws", A), NULL]
+    assert f(*args(r=0)) == INVALID
+    assert f(*args(r=65)) == INVALID
+    assert f(*args(K=40)) == SHAPE
+    assert f(*args(ws=None)) == INVALID
+    assert f(*args(ws=MIS)) == ALIGN
+
+
+def test_q8_0_rejects():
+    assert lib.q8_0_quantize(A, -1, A, NULL) == INVALID
+    assert lib.q8_0_quantize(NULL, 5, A, NULL) == INVALID
+    assert lib.q8_0_quantize(MIS, 5, A, NULL) == ALIGN
+    assert lib.q8_0_dequantize(A, 5, MIS, NULL) == ALIGN
+    assert lib.q8_0_quantize(NULL, 0, NULL, NULL) == OK
+    assert lib.q8_0_dequantize(NULL, 0, NULL, NULL) == OK
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        w8.w8a8_quant_act_rowwise(x)
+    with pytest.raises(TypeError):
+        w8.w8a8_quant_act_rowwise(x.float())

@@ -1,0 +1,252 @@
+"""MI355X (gfx950) W8A8 quantized linear: Python binding of libw8a8.so.
+
+Argument marshalling only.  Every step of the path runs in the HIP kernels of
+the shared library (C ABI in include/w8a8.h); torch provides device memory and
+the current stream.  The functions carry the C names:
+
+  w8a8_quant_weight_tensorwise  tensor-wise int8 / e4m3 weight quantization
+  w8a8_quant_act_rowwise        row-wise (token-wise) activation quantization
+  w8a8_linear                   8-bit product + fused dequant epilogue -> bf16
+  w8a8_linear_backward_dx       dX = dY . W from quantized dY and W^T codes
+  w8a8_gemm_i32                 raw int32 accumulators (test export)
+  svdq_linear                   residual 8-bit product + bf16 low-rank branch
+  q8_0_quantize / q8_0_dequantize / q8_0_nbytes   GGUF Q8_0 blocks
+
+Codes are torch.int8 (int8) or torch.float8_e4m3fn (e4m3); bf16 tensors are
+torch.bfloat16; scales are float32.  Output tensors may be passed in (`out=`)
+or are allocated on the input's device.  Nothing falls back to the CPU: if the
+library is missing, importing this package raises.
+"""
+import ctypes
+import os
+import re
+
+import torch
+
+from .build import LIB as _LIB_PATH
+
+INT8 = 0
+FP8_E4M3 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "w8a8.h")
+
+
+class W8A8Error(RuntimeError):
+    """A non-OK status returned by the library."""
+
+
+def _load_library():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is not built; run `python -m w8a8_quantized_linear_quant_amd.build` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    sigs = {
+        "w8a8_status_str": (ctypes.c_char_p, [I]),
+        "w8a8_weight_workspace_bytes": (ctypes.c_size_t, [I64, I64]),
+        "w8a8_quant_weight_tensorwise": (I, [I, P, I64, I64, P, P, P, P, P]),
+        "w8a8_quant_act_rowwise": (I, [I, P, I64, I64, I64, P, I64, P, P]),
+        "w8a8_linear": (I, [I, P, P, P, P, P, I64, I64, I64, P, P]),
+        "w8a8_linear_backward_dx": (I, [I, P, P, P, P, I64, I64, I64, P, P]),
+        "w8a8_gemm_i32": (I, [P, P, I64, I64, I64, P, P]),
+        "svdq_workspace_bytes": (ctypes.c_size_t, [I64, I64]),
+        "svdq_linear": (I, [I, P, I64, I64, P, P, P, P, I64, P, I64, P, P, P, P, P]),
+        "q8_0_nbytes": (ctypes.c_size_t, [I64]),
+        "q8_0_quantize": (I, [P, I64, P, P]),
+        "q8_0_dequantize": (I, [P, I64, P, P]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load_library()
+
+
+def exported_names_in_header(path=HEADER):
+    """Function names the C header declares (used to check the exports)."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\(", text)) -
+                  {"if", "defined", "sizeof", "extern"})
+
+
+def library():
+    return _lib
+
+
+def _check(status):
+    if status != 0:
+        raise W8A8Error(_lib.w8a8_status_str(status).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _qtype_of(codes):
+    if codes.dtype == torch.int8:
+        return INT8
+    if codes.dtype == torch.float8_e4m3fn:
+        return FP8_E4M3
+    raise TypeError(f"codes must be torch.int8 or torch.float8_e4m3fn, got {codes.dtype}")
+
+
+def _code_dtype(qtype):
+    return torch.int8 if qtype == INT8 else torch.float8_e4m3fn
+
+
+def _need(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+
+
+# ------------------------------------------------------------------ weights
+def w8a8_weight_workspace_bytes(N, K):
+    return int(_lib.w8a8_weight_workspace_bytes(N, K))
+
+
+def w8a8_quant_weight_tensorwise(w, qtype=INT8, transposed=False, out=None, out_t=None, scale=None,
+                                 workspace=None):
+    """w: bf16 [N, K].  Returns (codes [N, K], codes^T [K, N] or None, scale f32 [1])."""
+    _need(w, torch.bfloat16, "w")
+    w = w.contiguous()
+    N, K = w.shape
+    dev = w.device
+    wq = out if out is not None else torch.empty((N, K), dtype=_code_dtype(qtype), device=dev)
+    wq_t = out_t if out_t is not None else (
+        torch.empty((K, N), dtype=_code_dtype(qtype), device=dev) if transposed else None)
+    s = scale if scale is not None else torch.empty(4, dtype=torch.float32, device=dev)
+    ws = workspace if workspace is not None else torch.empty(
+        w8a8_weight_workspace_bytes(N, K), dtype=torch.uint8, device=dev)
+    _check(_lib.w8a8_quant_weight_tensorwise(qtype, _ptr(w), N, K, _ptr(wq), _ptr(wq_t), _ptr(s), _ptr(ws),
+                                             _stream(dev)))
+    return wq, wq_t, s[:1]
+
+
+# -------------------------------------------------------------- activations
+def w8a8_quant_act_rowwise(x, qtype=INT8, ldq=None, out=None, scale=None):
+    """x: bf16 [M, K] (row stride may exceed K).  Returns (codes [M, ldq], scales f32 [M])."""
+    _need(x, torch.bfloat16, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    M, K = x.shape
+    if M > 0 and (x.stride(0) % 8 != 0 or x.data_ptr() % 16 != 0):
+        # rows must start on 16-byte boundaries: copy into a padded buffer
+        padded = torch.zeros((M, K + (-K) % 8), dtype=x.dtype, device=x.device)
+        padded[:, :K] = x
+        x = padded
+    ldx = x.stride(0) if M > 1 else K + (-K) % 8
+    ldq = ldq if ldq is not None else K + (-K) % 16
+    dev = x.device
+    xq = out if out is not None else torch.empty((M, ldq), dtype=_code_dtype(qtype), device=dev)
+    s = scale if scale is not None else torch.empty(M, dtype=torch.float32, device=dev)
+    _check(_lib.w8a8_quant_act_rowwise(qtype, _ptr(x), M, K, ldx, _ptr(xq), ldq, _ptr(s), _stream(dev)))
+    return xq, s
+
+
+# --------------------------------------------------------------- the linear
+def w8a8_linear(xq, x_scale, wq, w_scale, bias=None, out=None):
+    """Dequantized 8-bit linear.  xq [M, K], wq [N, K] codes (same dtype) -> bf16 [M, N]."""
+    qt = _qtype_of(xq)
+    if wq.dtype != xq.dtype:
+        raise TypeError("xq and wq must hold the same code type")
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("xq and wq must share K")
+    _need(x_scale, torch.float32, "x_scale")
+    _need(w_scale, torch.float32, "w_scale")
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _check(_lib.w8a8_linear(qt, _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(bias), M, N, K, _ptr(y),
+                            _stream(xq.device)))
+    return y
+
+
+def w8a8_linear_backward_dx(dyq, dy_scale, wq_t, w_scale, out=None):
+    """dX = dY . W.  dyq [M, N] codes, wq_t [K, N] transposed weight codes -> bf16 [M, K]."""
+    qt = _qtype_of(dyq)
+    if wq_t.dtype != dyq.dtype:
+        raise TypeError("dyq and wq_t must hold the same code type")
+    M, N = dyq.shape
+    K = wq_t.shape[0]
+    if wq_t.shape[1] != N:
+        raise ValueError("dyq and wq_t must share N")
+    dx = out if out is not None else torch.empty((M, K), dtype=torch.bfloat16, device=dyq.device)
+    _check(_lib.w8a8_linear_backward_dx(qt, _ptr(dyq), _ptr(dy_scale), _ptr(wq_t), _ptr(w_scale), M, N, K,
+                                        _ptr(dx), _stream(dyq.device)))
+    return dx
+
+
+def w8a8_gemm_i32(xq, wq, out=None):
+    """Raw int32 accumulators of the int8 product: xq [M, K] @ wq[N, K]^T."""
+    _need(xq, torch.int8, "xq")
+    _need(wq, torch.int8, "wq")
+    M, K = xq.shape
+    N = wq.shape[0]
+    acc = out if out is not None else torch.empty((M, N), dtype=torch.int32, device=xq.device)
+    _check(_lib.w8a8_gemm_i32(_ptr(xq), _ptr(wq), M, N, K, _ptr(acc), _stream(xq.device)))
+    return acc
+
+
+# ------------------------------------------------------------------ SVDQuant
+def svdq_workspace_bytes(M, r):
+    return int(_lib.svdq_workspace_bytes(M, r))
+
+
+def svdq_linear(x, rq, r_scale, l1, l2, bias=None, out=None, xq_out=None, x_scale_out=None, workspace=None):
+    """x bf16 [M, K]; rq residual codes [N, K]; l1 bf16 [r, K]; l2 bf16 [N, r].
+    Returns (y bf16 [M, N], xq [M, K], x_scale [M])."""
+    qt = _qtype_of(rq)
+    _need(x, torch.bfloat16, "x")
+    _need(l1, torch.bfloat16, "l1")
+    _need(l2, torch.bfloat16, "l2")
+    x = x.contiguous()
+    M, K = x.shape
+    N = rq.shape[0]
+    r = l1.shape[0]
+    dev = x.device
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    xq = xq_out if xq_out is not None else torch.empty((M, K), dtype=rq.dtype, device=dev)
+    sx = x_scale_out if x_scale_out is not None else torch.empty(M, dtype=torch.float32, device=dev)
+    ws = workspace if workspace is not None else torch.empty(max(svdq_workspace_bytes(M, r), 16),
+                                                             dtype=torch.uint8, device=dev)
+    _check(_lib.svdq_linear(qt, _ptr(x), M, K, _ptr(rq), _ptr(r_scale), _ptr(l1.contiguous()),
+                            _ptr(l2.contiguous()), r, _ptr(bias), N, _ptr(y), _ptr(xq), _ptr(sx), _ptr(ws),
+                            _stream(dev)))
+    return y, xq, sx
+
+
+# ---------------------------------------------------------------------- Q8_0
+def q8_0_nbytes(n):
+    return int(_lib.q8_0_nbytes(n))
+
+
+def q8_0_quantize(x, out=None):
+    """x f32 (any shape, contiguous) -> uint8 [q8_0_nbytes(x.numel())] GGUF Q8_0 blocks."""
+    _need(x, torch.float32, "x")
+    x = x.contiguous()
+    n = x.numel()
+    blocks = out if out is not None else torch.empty(max(q8_0_nbytes(n), 16), dtype=torch.uint8, device=x.device)
+    _check(_lib.q8_0_quantize(_ptr(x), n, _ptr(blocks), _stream(x.device)))
+    return blocks[:q8_0_nbytes(n)]
+
+
+def q8_0_dequantize(blocks, n, out=None):
+    """blocks uint8 (>= q8_0_nbytes(n) bytes) -> f32 [n]."""
+    _need(blocks, torch.uint8, "blocks")
+    y = out if out is not None else torch.empty(max(n, 4), dtype=torch.float32, device=blocks.device)
+    _check(_lib.q8_0_dequantize(_ptr(blocks), n, _ptr(y), _stream(blocks.device)))
+    return y[:n]

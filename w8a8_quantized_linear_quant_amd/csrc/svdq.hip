@@ -1,0 +1,135 @@
+// svdq.hip -- SVDQuant-style linear: 8-bit product of the quantized residual
+// plus a bf16 low-rank branch.
+//
+// OneTrainer PR #1034 "SVDQuant" applies SVDQuant to every quant type; the
+// wiki's SVDQuant entry keeps the low-rank factors in bfloat16 at rank 16-32.
+// W ~ L2 . L1 + R: the residual R is quantized tensor-wise (as any W8A8
+// weight), the factors are not quantized.  Forward:
+//   y = dequant(codes(X) . codes(R)) + (X . L1^T) . L2^T + bias.
+//
+// Launches: (1) the row-wise act-quant kernel (X -> codes, row scales);
+// (2) the down-projection u = X . L1^T on the bf16 MFMA, written to the
+// workspace as two bf16 halves (u = hi + lo keeps ~16 significant bits, so
+// the up-projection does not round u to 8 bits); (3) the 8-bit product whose
+// epilogue adds hi . L2^T + lo . L2^T with the bf16 MFMA before the bias.
+#include "internal.hpp"
+
+namespace w8a8 {
+namespace {
+
+constexpr int kRows = 16;      // rows of X per workgroup (one 16x16x32 MFMA row block)
+constexpr int kThreads = 256;  // 4 waves split the K steps
+constexpr int kMaxRp = 64;
+
+typedef __bf16 v8bf_t __attribute__((ext_vector_type(8)));
+
+// u[m, j] = sum_k x[m, k] l1[j, k] for 16 rows; wave w takes the 32-wide k
+// steps w, w + 4, ...; partial sums meet in LDS.
+__global__ __launch_bounds__(kThreads) void svdq_down_kernel(const uint16_t *__restrict__ x, int M, int K,
+                                                             const uint16_t *__restrict__ l1, int r, int rp,
+                                                             uint16_t *__restrict__ uhi, uint16_t *__restrict__ ulo) {
+    __shared__ float part[4][kRows][kMaxRp + 1];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int m0 = blockIdx.x * kRows;
+    const int row = m0 + (lane & 15);
+    const int kq = (lane >> 4) * 8;  // this lane's 8 k values within a step
+    const int nsteps = (K + 31) / 32;
+    const int jblocks = rp / 16;
+
+    v4f acc[kMaxRp / 16];
+#pragma unroll
+    for (int b = 0; b < kMaxRp / 16; ++b) acc[b] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    for (int s = wave; s < nsteps; s += 4) {
+        const int k = s * 32 + kq;
+        v8bf_t a;
+        if (row < M && k + 8 <= K) {
+            a = *reinterpret_cast<const v8bf_t *>(x + (size_t)row * K + k);
+        } else {
+            uint16_t z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+            a = __builtin_bit_cast(v8bf_t, z);
+        }
+#pragma unroll
+        for (int b = 0; b < kMaxRp / 16; ++b) {
+            if (b >= jblocks) break;
+            const int j = b * 16 + (lane & 15);
+            v8bf_t bv;
+            if (j < r && k + 8 <= K) {
+                bv = *reinterpret_cast<const v8bf_t *>(l1 + (size_t)j * K + k);
+            } else {
+                uint16_t z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                bv = __builtin_bit_cast(v8bf_t, z);
+            }
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bv, acc[b], 0, 0, 0);
+        }
+    }
+    // C layout of the 16x16 MFMA: lane l, element i -> row 4(l/16) + i, col l%16.
+#pragma unroll
+    for (int b = 0; b < kMaxRp / 16; ++b) {
+        if (b >= jblocks) break;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[wave][4 * (lane >> 4) + i][b * 16 + (lane & 15)] = acc[b][i];
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < kRows * rp; idx += kThreads) {
+        const int rr = idx / rp, j = idx % rp;
+        const int m = m0 + rr;
+        if (m >= M) continue;
+        const float u = part[0][rr][j] + part[1][rr][j] + part[2][rr][j] + part[3][rr][j];
+        const uint32_t hi = f32_to_bf16_bits(u);
+        const uint32_t lo = f32_to_bf16_bits(u - bf16_bits_to_f32(hi));
+        uhi[(size_t)m * rp + j] = (uint16_t)hi;
+        ulo[(size_t)m * rp + j] = (uint16_t)lo;
+    }
+}
+
+inline int64_t round_up16(int64_t r) { return (r + 15) / 16 * 16; }
+
+}  // namespace
+}  // namespace w8a8
+
+extern "C" size_t svdq_workspace_bytes(int64_t M, int64_t r) {
+    if (M < 0 || r < 1 || r > w8a8::kMaxRp) return 0;
+    return (size_t)(2 * M * w8a8::round_up16(r) * sizeof(uint16_t));
+}
+
+extern "C" w8a8_status svdq_linear(w8a8_qtype qtype, const uint16_t *x, int64_t M, int64_t K, const void *rq,
+                                   const float *r_scale, const uint16_t *l1, const uint16_t *l2, int64_t r,
+                                   const uint16_t *bias, int64_t N, uint16_t *y, void *xq_out, float *x_scale_out,
+                                   void *workspace, hipStream_t stream) {
+    using namespace w8a8;
+    if (!valid_qtype(qtype) || r < 1 || r > kMaxRp) return W8A8_ERR_INVALID_ARG;
+    w8a8_status st = gemm_check(xq_out, rq, M, N, K, y);
+    if (st != W8A8_OK) return st;
+    st = act_quant_check(qtype, x, M, K, K, xq_out, K, x_scale_out);
+    if (st != W8A8_OK) return st;
+    if (M > 0 && N > 0 && (!r_scale || !l1 || !l2 || !workspace)) return W8A8_ERR_INVALID_ARG;
+    if (!aligned16(r_scale) || !aligned16(l1) || !aligned16(l2) || !aligned16(bias) || !aligned16(workspace))
+        return W8A8_ERR_ALIGN;
+    if (M == 0) return W8A8_OK;
+    st = act_quant_launch(qtype, x, M, K, K, xq_out, K, x_scale_out, stream);
+    if (st != W8A8_OK || N == 0) return st;
+    const int rp = (int)round_up16(r);
+    uint16_t *uhi = static_cast<uint16_t *>(workspace);
+    uint16_t *ulo = uhi + (size_t)M * rp;
+    const int grid = (int)((M + kRows - 1) / kRows);
+    svdq_down_kernel<<<grid, kThreads, 0, stream>>>(x, (int)M, (int)K, l1, (int)r, rp, uhi, ulo);
+    st = launch_status();
+    if (st != W8A8_OK) return st;
+    GemmArgs a = {};
+    a.xq = static_cast<const uint8_t *>(xq_out);
+    a.wq = static_cast<const uint8_t *>(rq);
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.sx = x_scale_out;
+    a.sw = r_scale;
+    a.bias = bias;
+    a.out = y;
+    a.uhi = uhi;
+    a.ulo = ulo;
+    a.l2 = l2;
+    a.r = (int)r;
+    a.rp = rp;
+    return gemm_launch(qtype, kEpiLowRank, a, stream);
+}
