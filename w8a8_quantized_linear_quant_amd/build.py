@@ -18,7 +18,7 @@ HEADERS = ["common.hpp", "internal.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
-    "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
+    "-O3", "-std=c++20", "-fPIC", "--offload-arch=gfx950",
     # packed-f32 instructions stay off: hipcc would otherwise form them from
     # ordinary float code.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

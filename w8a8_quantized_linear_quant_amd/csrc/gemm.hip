@@ -28,34 +28,64 @@
 //  * Tiles are numbered so that consecutive workgroups on one XCD (hardware
 //    dispatches workgroup i to XCD i % 8) share operand rows in that XCD's L2.
 #include <type_traits>
+#include <utility>
 
 #include "internal.hpp"
 
 namespace w8a8 {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 128;
+constexpr int BM = 256, BN = 256;
 constexpr int kThreads = 256;
-constexpr int kOpBytes = 256 * BK;           // one operand tile per stage: 32 KB
-constexpr int kStageBytes = 2 * kOpBytes;    // X tile then W tile
-constexpr int kGroupM = 4;                   // tile-ordering group height
+#ifndef W8A8_GEMM_GROUP_M
+#define W8A8_GEMM_GROUP_M 4
+#endif
+constexpr int kGroupM = W8A8_GEMM_GROUP_M;  // tile-ordering group height
 constexpr int kXcds = 8;
+
+#ifndef W8A8_GEMM_BK
+#define W8A8_GEMM_BK 64  // bytes of K per LDS stage
+#endif
+#ifndef W8A8_GEMM_NST
+#define W8A8_GEMM_NST 4  // LDS stages (loads run NST - 1 stages ahead)
+#endif
+constexpr int BK = W8A8_GEMM_BK;
+constexpr int NST = W8A8_GEMM_NST;
+constexpr int kOpBytes = 256 * BK;         // one operand tile per stage
+constexpr int kStageBytes = 2 * kOpBytes;  // X tile then W tile
+constexpr int kChunks = BK / 16;           // 16-byte chunks per row
+constexpr int kRowsPerLoad = 64 / kChunks; // rows one wave-wide 1 KB load covers
+constexpr int kLoadsPerOp = 64 / kRowsPerLoad;  // per wave and operand: 64 rows
+constexpr int kLoadsPerStage = 2 * kLoadsPerOp;
+constexpr int kImmLoads = kLoadsPerOp < 4 ? kLoadsPerOp : 4;  // loads per M0 value (immediate offsets < 4 KB)
+constexpr int kOutWaveBytes = 32 * 256;    // epilogue staging per wave
+static_assert(NST >= 3 && NST <= 4, "3..4 LDS stages");
+static_assert(NST * kStageBytes + 4 * kOutWaveBytes <= 160 * 1024, "LDS budget");
+static_assert((NST - 1) * kLoadsPerStage <= 63, "vmcnt range");
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
-__device__ __forceinline__ int swz(int row) { return row & 7; }
+// XOR swizzle of the 16-byte chunk index by row, chosen so that the fragment
+// reads of 16 consecutive rows (same logical chunk) spread over distinct bank
+// groups whether the LDS serves 8 or 16 lanes of a 128-bit read per cycle.
+// It depends on row % 16 only, so it is the same for every 32-row block.
+__device__ __forceinline__ int swz(int row) {
+    if constexpr (kChunks == 8) return (row & 7) ^ ((row >> 3) & 1);
+    else return ((row >> 1) ^ (row >> 2)) & 3;
+}
 
 struct TileCoord {
     int m0, n0;
 };
 
-__device__ __forceinline__ TileCoord tile_coord(int tiles_m, int tiles_n) {
+__device__ __forceinline__ TileCoord tile_coord(int tile, int tiles_m, int tiles_n) {
     const int nt = tiles_m * tiles_n;
-    int bid = blockIdx.x;
-    // XCD-major renumbering: hardware sends workgroup b to XCD b % 8; give
-    // each XCD a contiguous range of logical tiles.
+    // XCD-major renumbering: hardware sends workgroup b to XCD b % 8, and a
+    // persistent workgroup b takes tiles b, b + grid, ... (grid a multiple of
+    // 8 when it is the CU count); give each XCD a contiguous range of logical
+    // tiles so that the workgroups of one XCD share operand panels in its L2.
     const int per = nt / kXcds;
-    int t = bid < per * kXcds ? (bid % kXcds) * per + bid / kXcds : bid;
+    const int t = tile < per * kXcds ? (tile % kXcds) * per + tile / kXcds : tile;
     // grouped order: kGroupM tile-rows advance together along N
     const int group = kGroupM * tiles_n;
     const int g = t / group;
@@ -68,237 +98,435 @@ __device__ __forceinline__ TileCoord tile_coord(int tiles_m, int tiles_n) {
     return c;
 }
 
-template <int QT, int EPI>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStageBytes];
-
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const TileCoord tc = tile_coord(tiles_m, tiles_n);
-    const int K = p.K;
-
-    // Buffer descriptors starting at the tile's first row; rows past M (N)
-    // fall outside num_records and read as zero.
-    const int rows_x = min(p.M - tc.m0, BM), rows_w = min(p.N - tc.n0, BN);
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(p.xq + (size_t)tc.m0 * K), (short)0, rows_x * K, kBufferRsrcWord3);
-    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(p.wq + (size_t)tc.n0 * K), (short)0, rows_w * K, kBufferRsrcWord3);
-
-    // Global -> LDS mapping: wave w fills rows [64w, 64w+64) of each operand
-    // tile, 8 rows (1 KB) per instruction; lane l lands at LDS byte 16 l of
-    // that KB, i.e. row 8i + l/8, physical chunk l%8 = logical chunk ^ swz.
-    int goff[8], gcol[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = wave * 64 + i * 8 + (lane >> 3);
-        const int c = (lane & 7) ^ swz(row);
-        gcol[i] = c * 16;
-        goff[i] = row * K + c * 16;
-    }
-    const int ktiles = (K + BK - 1) / BK;
-
-    auto load_stage = [&](uint8_t *stage, int kt) {
-        const int k0 = kt * BK;
-        const bool full = k0 + BK <= K;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int o = full ? goff[i] + k0 : (k0 + gcol[i] < K ? goff[i] + k0 : kOobOffset);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(stage + (wave * 64 + i * 8) * BK), 16, o, 0, 0,
-                                                     0);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int o = full ? goff[i] + k0 : (k0 + gcol[i] < K ? goff[i] + k0 : kOobOffset);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, (lds_ptr_t)(stage + kOpBytes + (wave * 64 + i * 8) * BK),
-                                                     16, o, 0, 0, 0);
-        }
-    };
-
-    // Fragment read offsets: lane row = l & 31 within a 32-row block (so
-    // swz(row) = l & 7); the k-chunk depends on the step.
-    const int lrow = lane & 31, half = lane >> 5, sz = lane & 7;
-    typedef typename std::conditional<QT == W8A8_INT8, v16i, v16f>::type acc_t;
-    acc_t acc[4][4];
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[a][b][e] = 0;
-
-    auto compute_stage = [&](const uint8_t *stage) {
-        const uint8_t *xs = stage + (wm * 128) * BK;            // X rows of this wave
-        const uint8_t *ws = stage + kOpBytes + (wn * 128) * BK;  // W rows of this wave
-        if constexpr (QT == W8A8_INT8) {
-#pragma unroll
-            for (int kk = 0; kk < BK / 32; ++kk) {
-                const int off = lrow * BK + ((((kk * 2) + half) ^ sz) << 4);
-                v4i af[4], bf[4];
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb) af[nb] = *reinterpret_cast<const v4i *>(ws + nb * 32 * BK + off);
-#pragma unroll
-                for (int mb = 0; mb < 4; ++mb) bf[mb] = *reinterpret_cast<const v4i *>(xs + mb * 32 * BK + off);
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-                    for (int mb = 0; mb < 4; ++mb)
-                        acc[nb][mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[nb], bf[mb], acc[nb][mb], 0, 0, 0);
-            }
+// u . l2^T added to a 32x32 output block (rows n of l2, columns m of u) on
+// the bf16 MFMA, u as hi + lo bf16 halves; C layout as the 8-bit product.
+__device__ __forceinline__ v16f low_rank_add(const GemmArgs &p, v16f v, int nbase, int mbase, int lrow, int half) {
+    const int nrow = nbase + lrow, m = mbase + lrow;
+    for (int ks = 0; ks < p.rp; ks += 16) {
+        const int j0 = ks + half * 8;
+        uint16_t ta[8];
+        if (nrow < p.N && (p.r & 7) == 0 && j0 + 8 <= p.r) {
+            *reinterpret_cast<v4u *>(ta) = *reinterpret_cast<const v4u *>(p.l2 + (size_t)nrow * p.r + j0);
         } else {
 #pragma unroll
-            for (int kk = 0; kk < BK / 64; ++kk) {
-                const int c0 = kk * 4 + half * 2;
-                const int off0 = lrow * BK + ((c0 ^ sz) << 4);
-                const int off1 = lrow * BK + (((c0 + 1) ^ sz) << 4);
-                v8i af[4], bf[4];
+            for (int i = 0; i < 8; ++i) ta[i] = (nrow < p.N && j0 + i < p.r) ? p.l2[(size_t)nrow * p.r + j0 + i] : 0;
+        }
+        const v8bf a = __builtin_bit_cast(v8bf, ta);
+        v4u zh = {0u, 0u, 0u, 0u}, zl = {0u, 0u, 0u, 0u};
+        if (m < p.M) {
+            zh = *reinterpret_cast<const v4u *>(p.uhi + (size_t)m * p.rp + j0);
+            zl = *reinterpret_cast<const v4u *>(p.ulo + (size_t)m * p.rp + j0);
+        }
+        v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, zh), v, 0, 0, 0);
+        v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, zl), v, 0, 0, 0);
+    }
+    return v;
+}
+
+// Compute units of the current device (queried once per device).
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
+template <int QT, int EPI>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m, int tiles_n) {
+    // One distinct array per stage, so the compiler can tell the LDS-DMA writes
+    // into one stage from the fragment reads of another and does not wait for
+    // the former before the latter.
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds2[NST > 2 ? kStageBytes : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds3[NST > 3 ? kStageBytes : 16];
+    // Epilogue staging: per wave 32 rows x 128 bf16 columns (256 B rows).
+    __shared__ __attribute__((aligned(1024))) uint8_t obuf[EPI == kEpiI32 ? 16 : 4 * kOutWaveBytes];
+    auto buf = [&](auto s) -> uint8_t * {
+        constexpr int S = decltype(s)::value;
+        if constexpr (S == 0) return lds0;
+        else if constexpr (S == 1) return lds1;
+        else if constexpr (S == 2) return lds2;
+        else return lds3;
+    };
+
+    const int lane = threadIdx.x & 63;
+    // wave index as a scalar, so LDS addresses derived from it stay in SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int K = p.K, M = p.M, N = p.N;
+    const int ntiles = tiles_m * tiles_n;
+    const int ktiles = (K + BK - 1) / BK;
+    // Every tile runs a multiple of NST stages; stages past the end of K load
+    // out-of-range offsets (zeros) and add nothing.  This keeps the loop free
+    // of branches and the LDS ring aligned to the start of every tile.
+    const int kt_end = (ktiles + NST - 1) / NST * NST;
+
+    // Global -> LDS mapping: wave w fills rows [64w, 64w+64) of each operand
+    // tile, kRowsPerLoad rows (1 KB) per instruction; lane l lands at LDS byte
+    // 16 l of that KB: row l / kChunks, physical chunk l % kChunks, which holds
+    // logical chunk (l % kChunks) ^ swz(row).
+    int goff[kLoadsPerOp], gcol[kLoadsPerOp];
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) {
-                    const v4i lo = *reinterpret_cast<const v4i *>(ws + nb * 32 * BK + off0);
-                    const v4i hi = *reinterpret_cast<const v4i *>(ws + nb * 32 * BK + off1);
-                    af[nb] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                }
+    for (int i = 0; i < kLoadsPerOp; ++i) {
+        const int row = wave * 64 + i * kRowsPerLoad + lane / kChunks;
+        const int c = (lane % kChunks) ^ swz(row);
+        gcol[i] = c * 16;
+        // the instruction's immediate offset (i KB, see load_part) is added to
+        // the global address as well as to the LDS address; take it back out
+        goff[i] = row * K + c * 16 - (i % kImmLoads) * 1024;
+    }
+
+    // ---- load cursor: the stage ring runs ahead across tile boundaries, so
+    // the next tile's first stages are in flight during this tile's epilogue.
+    int ld_tile = blockIdx.x, ld_kt = 0;
+    __amdgpu_buffer_rsrc_t rx, rw;
+    auto set_desc = [&]() {
+        // Descriptors start at the tile's first row; rows past M (N) fall
+        // outside num_records and read as zero.  Past the last tile every
+        // record is out of range, so the ring keeps its constant load count.
+        int rows_x = 0, rows_w = 0;
+        size_t bx = 0, bw = 0;
+        if (ld_tile < ntiles) {
+            const TileCoord c = tile_coord(ld_tile, tiles_m, tiles_n);
+            rows_x = min(M - c.m0, BM);
+            rows_w = min(N - c.n0, BN);
+            bx = (size_t)c.m0 * K;
+            bw = (size_t)c.n0 * K;
+        }
+        rx = __builtin_amdgcn_make_buffer_rsrc((void *)(p.xq + bx), (short)0, rows_x * K, kBufferRsrcWord3);
+        rw = __builtin_amdgcn_make_buffer_rsrc((void *)(p.wq + bw), (short)0, rows_w * K, kBufferRsrcWord3);
+    };
+    set_desc();
+    // Loads of one stage, issued in NP parts (part P of NP) so that their
+    // issue spreads over the k-steps of the stage being multiplied.
+    // One LDS-DMA instruction writes 1 KB at M0 + immediate offset + 16 * lane.
+    // Loads are grouped so that consecutive ones share M0 and differ only in
+    // the immediate offset (i KB, below 4 KB): rewriting M0 between LDS-DMA
+    // instructions stalls the issuing wave.
+    auto load_part = [&](uint8_t *stage, auto part_c, auto np_c) {
+        constexpr int P = decltype(part_c)::value, NP = decltype(np_c)::value;
+        constexpr int lo = P * kLoadsPerStage / NP, hi = (P + 1) * kLoadsPerStage / NP;
+        const int k0 = ld_kt * BK;
+        const bool full = k0 + BK <= K;
+        [&]<int... J>(std::integer_sequence<int, J...>) {
+            (([&] {
+                 constexpr int j = lo + J;
+                 constexpr int i = j % kLoadsPerOp;
+                 constexpr int grp = i / kImmLoads, imm = (i % kImmLoads) * 1024;
+                 const int o = full ? goff[i] + k0 : (k0 + gcol[i] < K ? goff[i] + k0 : kOobOffset);
+                 uint8_t *m0 = stage + (j < kLoadsPerOp ? 0 : kOpBytes) + wave * 64 * BK + grp * kImmLoads * 1024;
+                 __builtin_amdgcn_raw_ptr_buffer_load_lds(j < kLoadsPerOp ? rx : rw, (lds_ptr_t)m0, 16, o, 0, imm, 0);
+             }()),
+             ...);
+        }(std::make_integer_sequence<int, hi - lo>{});
+    };
+    // Move the load cursor to the next stage (outside the interleaved regions:
+    // crossing into the next tile branches and recomputes the descriptors).
+    auto advance_cursor = [&]() {
+        if (++ld_kt == kt_end) {
+            ld_kt = 0;
+            ld_tile += gridDim.x;
+            set_desc();
+        }
+    };
+
+    // MFMA fragments: lane row = l & 31 within a 32-row block (swz(row)
+    // depends on l & 15 only); int8 takes 16 bytes per lane per k-step of 32,
+    // e4m3 32 bytes per k-step of 64.
+    constexpr bool kInt8 = QT == W8A8_INT8;
+    constexpr int KSTEPS = kInt8 ? BK / 32 : BK / 64;
+    static_assert(KSTEPS >= 1, "stage too small for one MFMA k-step");
+    typedef typename std::conditional<kInt8, v4i, v8i>::type frag_t;
+    typedef typename std::conditional<kInt8, v16i, v16f>::type acc_t;
+    const int lrow = lane & 31, half = lane >> 5;
+    const int lsw = swz(lrow);
+
+    acc_t acc[4][4];
+    frag_t fa[2][4], fb[2][4];
+
+    auto read_frags = [&](const uint8_t *stage, int kk, frag_t *af, frag_t *bf) {
+        const uint8_t *xs = stage + (wm * 128) * BK;            // X rows of this wave
+        const uint8_t *ws = stage + kOpBytes + (wn * 128) * BK;  // W rows of this wave
+        if constexpr (kInt8) {
+            const int off = lrow * BK + (((kk * 2 + half) ^ lsw) << 4);
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb) {
-                    const v4i lo = *reinterpret_cast<const v4i *>(xs + mb * 32 * BK + off0);
-                    const v4i hi = *reinterpret_cast<const v4i *>(xs + mb * 32 * BK + off1);
-                    bf[mb] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                }
+            for (int b = 0; b < 4; ++b) af[b] = *reinterpret_cast<const v4i *>(ws + b * 32 * BK + off);
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb)
+            for (int b = 0; b < 4; ++b) bf[b] = *reinterpret_cast<const v4i *>(xs + b * 32 * BK + off);
+        } else {
+            const int c0 = kk * 4 + half * 2;
+            const int off0 = lrow * BK + ((c0 ^ lsw) << 4);
+            const int off1 = lrow * BK + (((c0 + 1) ^ lsw) << 4);
 #pragma unroll
-                    for (int mb = 0; mb < 4; ++mb)
-                        acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[nb], bf[mb], acc[nb][mb], 0,
-                                                                                      0, 0, 127, 0, 127);
+            for (int b = 0; b < 4; ++b) {
+                const v4i lo = *reinterpret_cast<const v4i *>(ws + b * 32 * BK + off0);
+                const v4i hi = *reinterpret_cast<const v4i *>(ws + b * 32 * BK + off1);
+                af[b] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const v4i lo = *reinterpret_cast<const v4i *>(xs + b * 32 * BK + off0);
+                const v4i hi = *reinterpret_cast<const v4i *>(xs + b * 32 * BK + off1);
+                bf[b] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             }
         }
     };
 
-    // Main loop: two LDS stages, loads of the next stage in flight while the
-    // current one is multiplied.
-    load_stage(lds0, 0);
-    int kt = 0;
-    for (; kt + 2 <= ktiles; kt += 2) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        load_stage(lds1, kt + 1);
-        compute_stage(lds0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        if (kt + 2 < ktiles) load_stage(lds0, kt + 2);
-        compute_stage(lds1);
-    }
-    if (kt < ktiles) {  // odd number of stages: the last one sits in lds0
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        compute_stage(lds0);
-    }
-
-    // ------------------------------------------------------------- epilogue
-    // Block (nb, mb), register 4j+i holds output row m = mbase + (l & 31) and
-    // column n = nbase + 8j + 4(l >> 5) + i.
-    const int M = p.M, N = p.N;
-    const int mw = tc.m0 + wm * 128, nw = tc.n0 + wn * 128;
-    if constexpr (EPI == kEpiI32) {
-        int32_t *out = static_cast<int32_t *>(p.out);
+    auto mfmas = [&](const frag_t *af, const frag_t *bf) {
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
             for (int mb = 0; mb < 4; ++mb) {
-                const int m = mw + mb * 32 + lrow;
-                if (m >= M) continue;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int n = nw + nb * 32 + 8 * j + 4 * half;
-                    int32_t *dst = out + (size_t)m * N + n;
-                    if ((N & 3) == 0 && n + 3 < N) {
-                        v4i v = {(int)acc[nb][mb][4 * j], (int)acc[nb][mb][4 * j + 1], (int)acc[nb][mb][4 * j + 2],
-                                 (int)acc[nb][mb][4 * j + 3]};
-                        *reinterpret_cast<v4i *>(dst) = v;
-                    } else {
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (n + i < N) dst[i] = (int)acc[nb][mb][4 * j + i];
-                    }
-                }
+                if constexpr (kInt8)
+                    acc[nb][mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[nb], bf[mb], acc[nb][mb], 0, 0, 0);
+                else
+                    acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[nb], bf[mb], acc[nb][mb], 0, 0,
+                                                                                  0, 127, 0, 127);
             }
-    } else {
+    };
+
+    // Interleave the memory instructions of a k-step with its 16 MFMAs so that
+    // their issue (the LDS-DMA loads especially) overlaps MFMA execution
+    // instead of stalling the wave in front of the matrix pipe.
+    constexpr int kDsPerStep = kInt8 ? 8 : 16;  // ds_read_b128 per fragment set
+    auto interleave = [&](auto nvm_c) {
+        constexpr int NVM = decltype(nvm_c)::value;
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+            (([&] {
+                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+                 constexpr int ds = (I + 1) * kDsPerStep / 16 - I * kDsPerStep / 16;
+                 if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0);  // DS reads
+                 constexpr int vm = (I + 1) * NVM / 16 - I * NVM / 16;
+                 if constexpr (vm > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm, 0);  // VMEM reads
+             }()),
+             ...);
+        }(std::make_integer_sequence<int, 16>{});
+    };
+
+    // Within a stage the fragments of k-step kk+1 are read while the MFMAs of
+    // step kk run.  At the last step of a stage: wait until the next stage
+    // has landed and every wave is done with this one (barrier), refill this
+    // buffer with the stage NST ahead, read the first fragments of the next
+    // stage, then issue the last MFMAs.
+    // Stage kt lives in buffer kt % NST.  While stage kt is multiplied, the
+    // loads of stage kt + NST - 1 go into the buffer stage kt - 1 used (free
+    // since the barrier that ended stage kt - 1), one part per k-step.
+    // Within a stage the fragments of k-step kk+1 are read while the MFMAs of
+    // step kk run.  Before the last k-step: wait until stage kt+1 has landed
+    // and every wave is done reading stage kt (barrier), then read the first
+    // fragments of stage kt+1 and issue the last MFMAs of stage kt.
+    constexpr int kParts = KSTEPS;
+    constexpr int kPerPart = kLoadsPerStage / kParts;
+    static_assert(kLoadsPerStage % kParts == 0, "loads split evenly over k-steps");
+    // loads still allowed in flight when stage kt+1 must be complete: stages
+    // kt+2 .. kt+NST-2 whole, and the parts of stage kt+NST-1 issued so far
+    constexpr int kPending = (NST - 3) * kLoadsPerStage + (kParts - 1) * kPerPart;
+    auto run_stage = [&](auto sc) {
+        constexpr int S = decltype(sc)::value;
+        uint8_t *cur = buf(sc);
+        uint8_t *nxt = buf(std::integral_constant<int, (S + 1) % NST>{});
+        uint8_t *refill = buf(std::integral_constant<int, (S + NST - 1) % NST>{});
+        [&]<int... KK>(std::integer_sequence<int, KK...>) {
+            (([&] {
+                 constexpr int kk = KK;
+                 constexpr int P = (S * KSTEPS + kk) & 1;
+                 if constexpr (kk + 1 < KSTEPS) {
+                     __builtin_amdgcn_sched_barrier(0);
+                     read_frags(cur, kk + 1, fa[P ^ 1], fb[P ^ 1]);
+                     load_part(refill, std::integral_constant<int, kk>{}, std::integral_constant<int, kParts>{});
+                     mfmas(fa[P], fb[P]);
+                     interleave(std::integral_constant<int, kPerPart>{});
+                     __builtin_amdgcn_sched_barrier(0);
+                 } else {
+                     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPending) : "memory");
+                     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                     // a bare barrier: __syncthreads() would add a release fence,
+                     // i.e. a wait for every load in flight, prefetches included
+                     asm volatile("s_barrier" ::: "memory");
+                     __builtin_amdgcn_sched_barrier(0);
+                     load_part(refill, std::integral_constant<int, kk>{}, std::integral_constant<int, kParts>{});
+                     read_frags(nxt, 0, fa[P ^ 1], fb[P ^ 1]);
+                     mfmas(fa[P], fb[P]);
+                     interleave(std::integral_constant<int, kPerPart>{});
+                     __builtin_amdgcn_sched_barrier(0);
+                 }
+             }()),
+             ...);
+        }(std::make_integer_sequence<int, KSTEPS>{});
+        advance_cursor();
+    };
+    static_assert(NST % 2 == 0 || KSTEPS % 2 == 0, "fragment parity must restart at each stage group");
+
+    // Prologue: stages 0 .. NST-2 in flight, wait for stage 0.
+    [&]<int... S>(std::integer_sequence<int, S...>) {
+        ((load_part(buf(std::integral_constant<int, S>{}), std::integral_constant<int, 0>{},
+                    std::integral_constant<int, 1>{}),
+          advance_cursor()),
+         ...);
+    }(std::make_integer_sequence<int, NST - 1>{});
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 2) * kLoadsPerStage) : "memory");
+    asm volatile("s_barrier" ::: "memory");
+
+    // bf16 epilogue of one tile: y = bf16(acc * sx[m] * sw (+ u . l2^T) + bias[n]).
+    // Result rows go through this wave's LDS staging area (32 rows x 256 B,
+    // 16-byte chunks XOR-swizzled by row) and leave as 16-byte stores that
+    // cover whole 256-byte row segments.
+    auto bf16_epilogue = [&](auto interior_c, int mw, int nw) {
+        constexpr bool kIn = decltype(interior_c)::value;
         uint16_t *out = static_cast<uint16_t *>(p.out);
-        const float sw = p.sw[0];
+        uint8_t *ob = obuf + wave * kOutWaveBytes;
+        // Re-derive the lane indices here so the staging addresses are not
+        // hoisted out of the tile loop (they would stay live across the K
+        // loop and spill).
+        int el = lane;
+        asm volatile("" : "+v"(el));
+        const int erow = el & 31, ehalf = el >> 5;
         float tm[4];
+        uint2 bias2[4][4];
+        const float sw = p.sw[0];
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
-            const int m = mw + mb * 32 + lrow;
-            tm[mb] = m < M ? p.sx[m] * sw : 0.0f;
+            const int m = mw + mb * 32 + erow;
+            tm[mb] = (kIn || m < M) ? p.sx[m] * sw : 0.0f;
         }
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            float bias[4][4];
+        for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int n = nw + nb * 32 + 8 * j + 4 * half;
+                const int n = nw + nb * 32 + 8 * j + 4 * ehalf;
+                uint2 b = make_uint2(0u, 0u);
+                if (p.bias) {
+                    if (kIn || ((N & 3) == 0 && n < N)) {
+                        b = *reinterpret_cast<const uint2 *>(p.bias + n);
+                    } else {
+                        uint32_t w[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    bias[j][i] = (p.bias && n + i < N) ? bf16_bits_to_f32(p.bias[n + i]) : 0.0f;
+                        for (int i = 0; i < 4; ++i) w[i] = n + i < N ? p.bias[n + i] : 0u;
+                        b = make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
+                    }
+                }
+                bias2[nb][j] = b;
             }
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                const int m = mw + mb * 32 + lrow;
+        for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
                 v16f v;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) v[e] = (float)acc[nb][mb][e] * tm[mb];
-                if constexpr (EPI == kEpiLowRank) {
-                    // y += u . l2^T on the bf16 MFMA: A = l2 rows (n), B = u rows (m),
-                    // u = hi + lo in bf16.
-                    const int nrow = nw + nb * 32 + lrow;
-                    for (int ks = 0; ks < p.rp; ks += 16) {
-                        const int j0 = ks + half * 8;
-                        v8bf a, bh, bl;
-                        uint16_t ta[8];
-#pragma unroll
-                        for (int i = 0; i < 8; ++i)
-                            ta[i] = (nrow < N && j0 + i < p.r) ? p.l2[(size_t)nrow * p.r + j0 + i] : (uint16_t)0;
-                        a = __builtin_bit_cast(v8bf, ta);
-                        if (m < M) {
-                            bh = *reinterpret_cast<const v8bf *>(p.uhi + (size_t)m * p.rp + j0);
-                            bl = *reinterpret_cast<const v8bf *>(p.ulo + (size_t)m * p.rp + j0);
-                        } else {
-                            uint16_t z[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                            bh = __builtin_bit_cast(v8bf, z);
-                            bl = bh;
-                        }
-                        v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, v, 0, 0, 0);
-                        v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, v, 0, 0, 0);
-                    }
-                }
-                if (m >= M) continue;
+                if constexpr (EPI == kEpiLowRank) v = low_rank_add(p, v, nw + nb * 32, mw + mb * 32, erow, ehalf);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const int n = nw + nb * 32 + 8 * j + 4 * half;
-                    uint16_t *dst = out + (size_t)m * N + n;
-                    const float y0 = v[4 * j] + bias[j][0], y1 = v[4 * j + 1] + bias[j][1];
-                    const float y2 = v[4 * j + 2] + bias[j][2], y3 = v[4 * j + 3] + bias[j][3];
-                    if ((N & 3) == 0 && n + 3 < N) {
-                        uint2 pk = make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
-                        *reinterpret_cast<uint2 *>(dst) = pk;
-                    } else {
-                        const float yy[4] = {y0, y1, y2, y3};
+                    const uint2 bb = bias2[nb][j];
+                    const float y0 = v[4 * j] + bf16_bits_to_f32(bb.x & 0xFFFFu);
+                    const float y1 = v[4 * j + 1] + bf16_bits_to_f32(bb.x >> 16);
+                    const float y2 = v[4 * j + 2] + bf16_bits_to_f32(bb.y & 0xFFFFu);
+                    const float y3 = v[4 * j + 3] + bf16_bits_to_f32(bb.y >> 16);
+                    const int col = nb * 32 + 8 * j + 4 * ehalf;  // bf16 column within the wave tile
+                    const int chunk = (col >> 3) ^ (erow & 15);
+                    *reinterpret_cast<uint2 *>(ob + erow * 256 + chunk * 16 + (col & 7) * 2) =
+                        make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+                }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            // 32 rows x 16 chunks: 4 rows per wave-wide instruction
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (n + i < N) dst[i] = (uint16_t)f32_to_bf16_bits(yy[i]);
+            for (int it = 0; it < 8; ++it) {
+                const int r = it * 4 + (el >> 4), c = el & 15;
+                const v4u d = *reinterpret_cast<const v4u *>(ob + r * 256 + ((c ^ (r & 15)) << 4));
+                const int m = mw + mb * 32 + r, n = nw + c * 8;
+                uint16_t *dst = out + (size_t)m * N + n;
+                if constexpr (kIn) {
+                    __builtin_nontemporal_store(d, reinterpret_cast<v4u *>(dst));
+                } else if (m < M) {
+                    if ((N & 7) == 0 && n + 7 < N) {
+                        __builtin_nontemporal_store(d, reinterpret_cast<v4u *>(dst));
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 8; ++i)
+                            if (n + i < N) dst[i] = (uint16_t)(d[i >> 1] >> ((i & 1) * 16));
                     }
                 }
             }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         }
+    };
+
+    for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+        const TileCoord tc = tile_coord(tile, tiles_m, tiles_n);
+        const int mw = tc.m0 + wm * 128, nw = tc.n0 + wn * 128;
+        // Stage 0 of this tile has landed (prologue, or the last stage of the
+        // previous tile waited for it).  The copies of these fragments that
+        // the previous tile's last stage read are dead across its epilogue.
+        read_frags(lds0, 0, fa[0], fb[0]);
+
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[a][b][e] = 0;
+
+        for (int kt0 = 0; kt0 < kt_end; kt0 += NST) {
+            [&]<int... S>(std::integer_sequence<int, S...>) {
+                (run_stage(std::integral_constant<int, S>{}), ...);
+            }(std::make_integer_sequence<int, NST>{});
+        }
+
+        // --------------------------------------------------------- epilogue
+        // Block (nb, mb), register 4j+i holds output row m = mbase + (l & 31)
+        // and column n = nbase + 8j + 4(l >> 5) + i.
+        if constexpr (EPI == kEpiI32) {
+            int32_t *out = static_cast<int32_t *>(p.out);
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb) {
+                    const int m = mw + mb * 32 + lrow;
+                    if (m >= M) continue;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int n = nw + nb * 32 + 8 * j + 4 * half;
+                        int32_t *dst = out + (size_t)m * N + n;
+                        if ((N & 3) == 0 && n + 3 < N) {
+                            v4i v = {(int)acc[nb][mb][4 * j], (int)acc[nb][mb][4 * j + 1],
+                                     (int)acc[nb][mb][4 * j + 2], (int)acc[nb][mb][4 * j + 3]};
+                            *reinterpret_cast<v4i *>(dst) = v;
+                        } else {
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                if (n + i < N) dst[i] = (int)acc[nb][mb][4 * j + i];
+                        }
+                    }
+                }
+        } else {
+            // Interior tiles (all 256 rows and columns in range, N % 8 == 0)
+            // take a copy of the epilogue without any bounds checks.
+            const bool interior = tc.m0 + BM <= M && tc.n0 + BN <= N && (N & 7) == 0;
+            if (interior) bf16_epilogue(std::true_type{}, mw, nw);
+            else bf16_epilogue(std::false_type{}, mw, nw);
+        }
+        // The K loop counts VMEM operations in flight (vmcnt) on the premise
+        // that they are all stage loads; let this tile's stores drain first.
+        if constexpr (NST > 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
+    // Loads of the stages past the last tile (all out of range) may still be
+    // in flight; let them land before the workgroup ends.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 template <int QT, int EPI>
 void launch(const GemmArgs &a, hipStream_t stream) {
     const int tm = (a.M + BM - 1) / BM, tn = (a.N + BN - 1) / BN;
-    gemm_kernel<QT, EPI><<<tm * tn, kThreads, 0, stream>>>(a, tm, tn);
+    const int tiles = tm * tn;
+    const int grid = tiles < device_cu_count() ? tiles : device_cu_count();
+    gemm_kernel<QT, EPI><<<grid, kThreads, 0, stream>>>(a, tm, tn);
 }
 
 }  // namespace
