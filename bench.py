@@ -40,6 +40,8 @@ def _args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-rows", action="store_true", help="skip the per-row figures of the other paths")
     p.add_argument("--cpu-rows", type=int, default=96, help="rows of the oracle sample")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="also run one plain 512 MiB device copy (reference for HBM byte counters)")
     return p.parse_args()
 
 
@@ -183,6 +185,14 @@ def main():
     act = {"bound": "hbm", "achieved": round(aq_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
            "frac": round(aq_gbs / PEAK_HBM_GBS, 4), "us_per_launch": round(ms_aq * 1e3, 2),
            "algorithmic_bytes_per_launch": aq_bytes, "kernel": "act_quant_rowwise_kernel<int8>"}
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 29, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     rows = {} if args.no_rows else other_rows(w8, torch, workloads, args)
     for s in sets:

@@ -50,12 +50,13 @@ __device__ __forceinline__ uint2 quantize8(v4u d, float s, float r) {
         const float magic = 12582912.0f;
         uint32_t b[8];
 #pragma unroll
+        // The clamp to [-128, 127] of the definition cannot bind here:
+        // |x| <= absmax gives |x / s| <= 127 (1 + 2^-23), which rounds to at
+        // most 127.  The sign of zero does not matter for an integer code.
         for (int w = 0; w < 4; ++w) {
             float lo = __uint_as_float(d[w] << 16), hi = __uint_as_float(d[w] & 0xFFFF0000u);
-            float qlo = __builtin_amdgcn_fmed3f(quotient(lo, s, r), -128.0f, 127.0f);
-            float qhi = __builtin_amdgcn_fmed3f(quotient(hi, s, r), -128.0f, 127.0f);
-            b[2 * w] = __float_as_uint(qlo + magic);
-            b[2 * w + 1] = __float_as_uint(qhi + magic);
+            b[2 * w] = __float_as_uint(quotient_nosign(lo, s, r) + magic);
+            b[2 * w + 1] = __float_as_uint(quotient_nosign(hi, s, r) + magic);
         }
         // byte-gather: v_perm_b32 selects bytes of {src0, src1}; selector byte
         // 0..3 picks src1 bytes, 4..7 picks src0 bytes.
@@ -98,43 +99,62 @@ __device__ __forceinline__ void zero_pad(uint8_t *qrow, int K, int64_t ldq, int 
         *reinterpret_cast<uint2 *>(qrow + c) = make_uint2(0u, 0u);
 }
 
-template <int QT, int CPL>
+// A wave quantizes rows row0, row0 + stride, ... of X, two rows in flight:
+// the loads of the next row are issued before the current row is reduced,
+// quantized and stored, so reads, VALU work and writes overlap.
+template <int QT, int CPL, bool FULL>
 __global__ __launch_bounds__(256) void act_quant_rowwise_kernel(const uint16_t *__restrict__ x, int64_t M, int K,
                                                                 int64_t ldx, uint8_t *__restrict__ xq, int64_t ldq,
                                                                 float *__restrict__ scale) {
     constexpr float kQmax = QT == W8A8_INT8 ? 127.0f : 448.0f;
     const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
-    if (row >= M) return;
-    const uint16_t *xr = x + row * ldx;
+    const int64_t stride = (int64_t)gridDim.x * kRowsPerBlock;
     const int nchunks = (K + 7) >> 3;
 
-    v4u d[CPL];
-    uint32_t m2 = 0;
+    auto load = [&](v4u *d, int64_t row) {
+        const v4u *xr = reinterpret_cast<const v4u *>(x + row * ldx);
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        const int chunk = c * 64 + lane;
-        if (chunk < nchunks) {
-            d[c] = mask_tail(__builtin_nontemporal_load(reinterpret_cast<const v4u *>(xr) + chunk), chunk * 8, K);
-        } else {
-            d[c] = v4u{0u, 0u, 0u, 0u};
+        for (int c = 0; c < CPL; ++c) {
+            const int chunk = c * 64 + lane;
+            if constexpr (FULL)  // K == 512 CPL: every lane owns CPL whole chunks
+                d[c] = __builtin_nontemporal_load(xr + chunk);
+            else
+                d[c] = chunk < nchunks ? mask_tail(__builtin_nontemporal_load(xr + chunk), chunk * 8, K)
+                                       : v4u{0u, 0u, 0u, 0u};
         }
-    }
+    };
+    auto process = [&](const v4u *d, int64_t row) {
+        uint32_t m2 = 0;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) m2 = pk_max_u16(m2, chunk_absmax_bits(d[c]));
-    uint32_t mbits = (m2 & 0xFFFFu) > (m2 >> 16) ? (m2 & 0xFFFFu) : (m2 >> 16);
-    mbits = wave_max_u32(mbits);
-    const float s = absmax_scale(bf16_bits_to_f32(mbits), kQmax);
-    const float r = 1.0f / s;
-    if (lane == 0) scale[row] = s;
+        for (int c = 0; c < CPL; ++c) m2 = pk_max_u16(m2, chunk_absmax_bits(d[c]));
+        const uint32_t mbits = wave_max_u32(max(m2 & 0xFFFFu, m2 >> 16));
+        const float s = absmax_scale(bf16_bits_to_f32(mbits), kQmax);
+        const float r = 1.0f / s;
+        if (lane == 0) scale[row] = s;
+        uint8_t *qrow = xq + row * ldq;
+#pragma unroll
+        for (int c = 0; c < CPL; ++c) {
+            const int chunk = c * 64 + lane;
+            if (FULL || chunk < nchunks) *reinterpret_cast<uint2 *>(qrow + chunk * 8) = quantize8<QT>(d[c], s, r);
+        }
+        if (ldq > K) zero_pad(qrow, K, ldq, lane);
+    };
 
-    uint8_t *qrow = xq + row * ldq;
-#pragma unroll
-    for (int c = 0; c < CPL; ++c) {
-        const int chunk = c * 64 + lane;
-        if (chunk < nchunks) *reinterpret_cast<uint2 *>(qrow + chunk * 8) = quantize8<QT>(d[c], s, r);
+    int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (row >= M) return;
+    v4u a[CPL], b[CPL];
+    load(a, row);
+    while (true) {
+        const int64_t r1 = row + stride;
+        if (r1 < M) load(b, r1);
+        process(a, row);
+        if (r1 >= M) break;
+        const int64_t r2 = r1 + stride;
+        if (r2 < M) load(a, r2);
+        process(b, r1);
+        if (r2 >= M) break;
+        row = r2;
     }
-    if (ldq > K) zero_pad(qrow, K, ldq, lane);
 }
 
 // Rows too long for registers: absmax pass, then a quantize pass re-reading x.
@@ -165,11 +185,19 @@ __global__ __launch_bounds__(256) void act_quant_rowwise_2pass_kernel(const uint
 template <int QT>
 void launch_act_quant(const uint16_t *x, int64_t M, int K, int64_t ldx, uint8_t *xq, int64_t ldq, float *scale,
                       hipStream_t stream) {
-    const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock)), block(64 * kRowsPerBlock);
+    // Single-pass kernel: about two workgroups per CU, each wave walking
+    // rows with a stride of the whole grid (two rows in flight per wave).
+    const int64_t blocks = (M + kRowsPerBlock - 1) / kRowsPerBlock;
+    const int64_t cap = 2 * (int64_t)device_cu_count();
+    const dim3 grid((unsigned)(blocks < cap ? blocks : cap)), block(64 * kRowsPerBlock);
+    const dim3 grid2((unsigned)blocks);
     const int cpl = (((K + 7) / 8) + 63) / 64;  // 16-byte chunks per lane
 #define W8A8_ACTQ_CASE(N)                                                                             \
     if (cpl <= N) {                                                                                   \
-        act_quant_rowwise_kernel<QT, N><<<grid, block, 0, stream>>>(x, M, K, ldx, xq, ldq, scale);    \
+        if (K == 512 * N)                                                                             \
+            act_quant_rowwise_kernel<QT, N, true><<<grid, block, 0, stream>>>(x, M, K, ldx, xq, ldq, scale); \
+        else                                                                                          \
+            act_quant_rowwise_kernel<QT, N, false><<<grid, block, 0, stream>>>(x, M, K, ldx, xq, ldq, scale); \
         return;                                                                                       \
     }
     W8A8_ACTQ_CASE(1)
@@ -182,7 +210,7 @@ void launch_act_quant(const uint16_t *x, int64_t M, int K, int64_t ldx, uint8_t 
     W8A8_ACTQ_CASE(24)
     W8A8_ACTQ_CASE(32)
 #undef W8A8_ACTQ_CASE
-    act_quant_rowwise_2pass_kernel<QT><<<grid, block, 0, stream>>>(x, M, K, ldx, xq, ldq, scale);
+    act_quant_rowwise_2pass_kernel<QT><<<grid2, block, 0, stream>>>(x, M, K, ldx, xq, ldq, scale);
 }
 
 }  // namespace

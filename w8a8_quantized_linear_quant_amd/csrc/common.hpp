@@ -53,14 +53,21 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// Wave-wide max of a non-negative integer (wave64) via DPP-free xor shuffles.
+// Wave-wide max of a non-negative integer (wave64): DPP row shifts reduce
+// each 16-lane row into its lane 15, four lane reads combine the rows; the
+// result is wave-uniform.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        uint32_t o = __shfl_xor(v, off, 64);
-        v = v > o ? v : o;
-    }
-    return v;
+    // row_shr:n (dpp ctrl 0x110 + n); lanes shifted in from outside the row
+    // read 0 (bound_ctrl), which is neutral for a max of non-negative values
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, true));
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, true));
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+    const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 31);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 47);
+    const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+    return max(max(r0, r1), max(r2, r3));
 }
 
 // Absmax scale rule of every quantizer: 1e-10 floor, else absmax / QMAX (IEEE
@@ -73,12 +80,15 @@ __device__ __forceinline__ float absmax_scale(float amax, float qmax) {
 //   q0 = x r,  e = x - q0 s (exact with an FMA),  q = q0 + e r,
 // sign of zero taken from x.  Bit-identical to the IEEE quotient for every
 // bf16 x and every scale derived from a bf16 absmax (checked exhaustively on
-// the host), at 3 VALU ops instead of the ~10 of a full division.
-__device__ __forceinline__ float quotient(float x, float s, float r) {
+// the host), at 3 VALU ops instead of the ~10 of a full division (the sign
+// of zero aside, which the copysign restores).
+__device__ __forceinline__ float quotient_nosign(float x, float s, float r) {
     float q0 = x * r;
     float e = __builtin_fmaf(-q0, s, x);
-    float q = __builtin_fmaf(e, r, q0);
-    return __builtin_copysignf(q, x);
+    return __builtin_fmaf(e, r, q0);
+}
+__device__ __forceinline__ float quotient(float x, float s, float r) {
+    return __builtin_copysignf(quotient_nosign(x, s, r), x);
 }
 
 }  // namespace w8a8

@@ -123,18 +123,6 @@ __device__ __forceinline__ v16f low_rank_add(const GemmArgs &p, v16f v, int nbas
     return v;
 }
 
-// Compute units of the current device (queried once per device).
-int device_cu_count() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
-}
 
 template <int QT, int EPI>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m, int tiles_n) {
@@ -530,6 +518,19 @@ void launch(const GemmArgs &a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Compute units of the current device (queried once per device).
+int device_cu_count() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
 
 w8a8_status gemm_check(const void *xq, const void *wq, int64_t M, int64_t N, int64_t K, const void *out) {
     if (M < 0 || N < 0 || K < 0) return W8A8_ERR_INVALID_ARG;

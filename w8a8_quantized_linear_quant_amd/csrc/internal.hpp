@@ -29,6 +29,9 @@ struct GemmArgs {
     int r, rp;
 };
 
+// Compute units of the current device (queried once per device).
+int device_cu_count();
+
 w8a8_status gemm_check(const void *xq, const void *wq, int64_t M, int64_t N, int64_t K, const void *out);
 w8a8_status gemm_launch(w8a8_qtype qtype, GemmEpilogue epi, const GemmArgs &a, hipStream_t stream);
 
