@@ -153,8 +153,8 @@ w8a8_status w8a8_gemm_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t
 
 /* ------------------------------------------------------------------ SVDQuant */
 
-/* Bytes of device workspace svdq_linear needs: U, f32 [M, r] (two bf16
- * halves of it, hi and lo, [M, r] each). */
+/* Bytes of device workspace svdq_linear needs: U = X . L1^T as two bf16
+ * halves, hi and lo, [M, roundup(r, 16)] each.  0 if r is outside [1, 64]. */
 size_t svdq_workspace_bytes(int64_t M, int64_t r);
 
 /*
@@ -169,10 +169,11 @@ size_t svdq_workspace_bytes(int64_t M, int64_t r);
  *   projection, nn.Linear layout); l2 bf16 [N, r] (up-projection); bias bf16
  *   [N] or NULL; y bf16 [M, N]; xq_out codes [M, K]; x_scale_out f32 [M];
  *   workspace svdq_workspace_bytes(M, r) bytes.
- * Two launches: act-quant fused with the down-projection, then the 8-bit
- * product whose epilogue adds the up-projection (bf16 MFMA on a hi/lo bf16
- * split of u, so u keeps ~16 bits of precision).
- * Shape rules: as w8a8_linear; r in {16, 32, 48, 64}.
+ * Three launches: the row-wise act-quant, the down-projection (bf16 MFMA,
+ * u written as a hi/lo pair of bf16 halves so it keeps ~16 bits), then the
+ * 8-bit product whose epilogue adds the up-projection on the bf16 MFMA.
+ * Shape rules: as w8a8_linear (K % 16 == 0); 1 <= r <= 64, else
+ * W8A8_ERR_INVALID_ARG.
  */
 w8a8_status svdq_linear(w8a8_qtype qtype, const uint16_t *x, int64_t M, int64_t K, const void *rq,
                         const float *r_scale, const uint16_t *l1, const uint16_t *l2, int64_t r,
