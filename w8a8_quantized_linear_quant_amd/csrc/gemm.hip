@@ -9,24 +9,27 @@
 // this kernel's epilogue, so the int32/f32 accumulators never leave registers.
 //
 // CDNA4 design:
-//  * 256x256 output tile per workgroup, 4 waves in a 2x2 grid, each wave a
-//    128x128 sub-tile held as 4x4 blocks of 32x32 MFMA accumulators
-//    (v_mfma_i32_32x32x32_i8, or v_mfma_scale_f32_32x32x64_f8f6f4 with unit
-//    scales for e4m3): 256 accumulator registers per lane.
+//  * Persistent: one 256-thread workgroup per CU walks 256x256 output tiles,
+//    4 waves in a 2x2 grid, each wave a 128x128 sub-tile held as 4x4 blocks
+//    of 32x32 MFMA accumulators (v_mfma_i32_32x32x32_i8, or
+//    v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales for e4m3): 256
+//    accumulator registers per lane, one wave per SIMD.
 //  * Both operands are K-contiguous ("NT"), so every lane's MFMA fragment is
 //    a contiguous 16- or 32-byte run of one row.  The weight is the MFMA's A
 //    operand and the activations its B operand, so each lane ends up holding
-//    four consecutive output columns of one row: 8-byte bf16 stores.
-//  * K is consumed in 128-byte stages.  Stages go HBM -> LDS directly with
-//    buffer_load_dwordx4 ... lds (no register staging), double buffered in two
-//    separate LDS arrays so the loads of stage t+1 overlap the MFMAs of stage
-//    t.  Buffer loads past num_records read zero, which covers ragged M/N
-//    tails and (with an out-of-range offset) the ragged K tail.
-//  * Within a stage, 16-byte chunks of each 128-byte row are XOR-swizzled by
-//    the row index so the fragment reads of 8 consecutive rows hit 8 distinct
-//    bank groups.
-//  * Tiles are numbered so that consecutive workgroups on one XCD (hardware
-//    dispatches workgroup i to XCD i % 8) share operand rows in that XCD's L2.
+//    four consecutive output columns of one row.
+//  * K goes HBM -> LDS in BK-byte stages through a ring of NST buffers with
+//    buffer_load_dwordx4 ... lds (no register staging); the ring runs NST - 1
+//    stages ahead, across tile boundaries.  Buffer loads past num_records
+//    read zero, which covers ragged M/N tails and (with an out-of-range
+//    offset) the ragged K tail.
+//  * Within a stage, 16-byte chunks of each row are XOR-swizzled by the row
+//    index so the fragment reads of consecutive rows hit distinct banks.
+//  * Tiles are numbered so that the workgroups of one XCD (hardware sends
+//    workgroup i to XCD i % 8) share operand panels in that XCD's L2.
+//  * The epilogue scales, adds the bias, packs to bf16 and stages each
+//    32-row slice of a wave's sub-tile through LDS so that it leaves as
+//    16-byte stores covering 256-byte row segments.
 #include <type_traits>
 #include <utility>
 
