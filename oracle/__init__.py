@@ -55,6 +55,8 @@ def _load():
         "orc_q8_0_quantize": (I, [P, I64, P]),
         "orc_q8_0_dequantize": (I, [P, I64, P]),
         "orc_convert_array": (I, [I, P, I64, P]),
+        "orc_gguf_a8_requant_q8_0": (I, [I, P, I64, I64, P, P, P]),
+        "orc_linear_axiswise": (I, [I, P, P, P, P, P, I64, I64, I64, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -250,4 +252,32 @@ def q8_0_dequantize(blocks, n):
     assert b.size >= q8_0_nbytes(n)
     y = np.empty(n, np.float32)
     _check(_load().orc_q8_0_dequantize(_p(b), n, _p(y)), "q8_0_dequantize")
+    return y
+
+
+# ---------------------------------------------------------------- GGUF A8
+def gguf_a8_requant_q8_0(qtype, blocks, N, K):
+    """Q8_0 weight [N, K] (K % 32 == 0; row n = K / 32 blocks) -> (codes [N, K], scales f32 [N])."""
+    b = _c(blocks, np.uint8).ravel()
+    assert K % Q8_0_BLOCK == 0 and b.size >= N * (K // Q8_0_BLOCK) * Q8_0_BYTES
+    wq = np.empty((N, K), np.uint8)
+    s = np.empty(N, np.float32)
+    v = np.empty(max(K, 1), np.float32)
+    _check(_load().orc_gguf_a8_requant_q8_0(qtype, _p(b), N, K, _p(wq), _p(s), _p(v)), "gguf_a8_requant_q8_0")
+    return wq, s
+
+
+def linear_axiswise(qtype, xq, sx, wq, sw, bias=None):
+    """Dequantized 8-bit linear with per-output-channel weight scales sw [N] -> bf16 bits [M, N]."""
+    xq = _c(np.asarray(xq).view(np.uint8), np.uint8)
+    wq = _c(np.asarray(wq).view(np.uint8), np.uint8)
+    sx = _c(sx, np.float32)
+    sw = _c(sw, np.float32)
+    M, K = xq.shape
+    N = wq.shape[0]
+    assert wq.shape[1] == K and sx.shape == (M,) and sw.shape == (N,)
+    b = None if bias is None else _c(bias, np.uint16)
+    y = np.empty((M, N), np.uint16)
+    _check(_load().orc_linear_axiswise(qtype, _p(xq), _p(sx), _p(wq), _p(sw), _p(b), M, N, K, _p(y)),
+           "linear_axiswise")
     return y

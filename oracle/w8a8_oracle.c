@@ -28,7 +28,10 @@
  *    the stored f16 scale;
  *  - the dequantized linear output is bf16(acc * sx[m] * sw + bias[n]) with the
  *    right-hand side evaluated in double and rounded to bf16 once;
- *  - the SVDQuant branch adds (X . L1^T) . L2^T, both products in double.
+ *  - the SVDQuant branch adds (X . L1^T) . L2^T, both products in double;
+ *  - GGUF A8: the GGUF weight is Q8_0 (the one GGUF format the pages define),
+ *    "axis-wise" for the weight means one scale per output channel (row of
+ *    W [out, in]), and the row's values are the exact Q8_0 dequantization.
  *
  * Build: gcc -O2 -ffp-contract=off -fno-fast-math -shared -fPIC.  Every
  * rounding named below happens exactly once; exact sums run in int64 / double.
@@ -377,6 +380,53 @@ int orc_q8_0_dequantize(const uint8_t *blocks, int64_t n, float *y) {
         int8_t q = (int8_t)blk[2 + i % ORC_Q8_0_BLOCK];
         y[i] = (float)((double)q * orc_f16_to_f64(d));
     }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
+/* GGUF A8 int / GGUF A8 float (OneTrainer wiki "Quantization", "Technical"):  */
+/* the weight as stored in the GGUF file is re-quantized axis-wise to int8 or  */
+/* e4m3 -- one scale per output channel, i.e. per row n of W [N, K] -- and the */
+/* product runs in 8 bits on token-wise quantized activations.  Here the GGUF  */
+/* weight is Q8_0: row n is K / 32 consecutive 34-byte blocks (K % 32 == 0).   */
+/* ------------------------------------------------------------------------- */
+
+/* Re-quantization of one Q8_0 row per output channel: the row's values are
+ * the exact Q8_0 dequantization f32(q) * f32(d); s[n] = absmax scale of the row
+ * (1e-10 floor, QMAX 127 or 448); codes as the other quantizers (int8:
+ * clamp(rne(v / s)), e4m3: e4m3_rne(clamp(v / s, +-448))).  v_work: f32 [K]. */
+int orc_gguf_a8_requant_q8_0(int qtype, const uint8_t *blocks, int64_t N, int64_t K,
+                             uint8_t *wq, float *scale, float *v_work) {
+    if ((qtype != 0 && qtype != 1) || N < 0 || K < 0 || K % ORC_Q8_0_BLOCK != 0) return ORC_ERR;
+    const float qmax = qtype == 0 ? 127.0f : 448.0f;
+    const int64_t row_bytes = (K / ORC_Q8_0_BLOCK) * ORC_Q8_0_BYTES;
+    for (int64_t n = 0; n < N; ++n) {
+        if (orc_q8_0_dequantize(blocks + n * row_bytes, K, v_work) != ORC_OK) return ORC_ERR;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(v_work[k]);
+            if (a > amax) amax = a;
+        }
+        float s = orc_absmax_scale(amax, qmax);
+        scale[n] = s;
+        for (int64_t k = 0; k < K; ++k)
+            wq[n * K + k] = qtype == 0 ? (uint8_t)orc_code_int8(v_work[k], s) : orc_code_e4m3(v_work[k], s);
+    }
+    return ORC_OK;
+}
+
+/* Quantized linear with a per-output-channel weight scale:
+ * y[m, n] = bf16(acc[m, n] * sx[m] * sw[n] + bias[n]), in double, rounded once. */
+int orc_linear_axiswise(int qtype, const uint8_t *xq, const float *sx, const uint8_t *wq, const float *sw,
+                        const uint16_t *bias, int64_t M, int64_t N, int64_t K, uint16_t *y) {
+    if ((qtype != 0 && qtype != 1) || M < 0 || N < 0 || K < 0) return ORC_ERR;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = code_dot(qtype, xq + m * K, wq + n * K, K, 1);
+            double v = acc * (double)sx[m] * (double)sw[n];
+            if (bias) v += orc_bf16_to_f64(bias[n]);
+            y[m * N + n] = orc_f64_to_bf16(v);
+        }
     return ORC_OK;
 }
 
