@@ -279,6 +279,23 @@ def other_rows(w8, torch, workloads, args):
     res["q8_0_quantize_n16777221"] = {"us": round(ms * 1e3, 1), "GB/s": round(qbytes / ms / 1e6, 1)}
     ms = _time_launches(lambda i: w8.q8_0_dequantize(blob, n, out=out), iters, 3)
     res["q8_0_dequantize_n16777221"] = {"us": round(ms * 1e3, 1), "GB/s": round(qbytes / ms / 1e6, 1)}
+    del v, blob, out
+    # GGUF A8: Q8_0 weight [12288, 3072] -> per-channel int8 / e4m3, then the linear at the headline shape
+    d = workloads.gguf()
+    gb = torch.from_numpy(d["w_blocks"]).cuda()
+    x = _bf16(d["x"])
+    bb = _bf16(d["bias"])
+    y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    for qt, tag in ((w8.INT8, "int8"), (w8.FP8_E4M3, "fp8")):
+        wq = torch.empty((N, K), dtype=torch.int8 if qt == w8.INT8 else torch.float8_e4m3fn, device="cuda")
+        sw = torch.empty(N, dtype=torch.float32, device="cuda")
+        ms = _time_launches(lambda i: w8.gguf_a8_requant_q8_0(gb, N, K, qtype=qt, out=wq, scale=sw), iters, 3)
+        rbytes = 1.0 * gb.numel() + N * K + 4.0 * N  # blocks read once, codes and scales written
+        res[f"gguf_a8_requant_{tag}_N12288_K3072"] = {"us": round(ms * 1e3, 1), "GB/s": round(rbytes / ms / 1e6, 1)}
+        xq, sx = w8.w8a8_quant_act_rowwise(x, qtype=qt)
+        ms = _time_launches(lambda i: w8.gguf_a8_linear(xq, sx, wq, sw, bb, out=y), iters, 3)
+        res[f"gguf_a8_linear_{tag}_M4096_K3072_N12288"] = {"us": round(ms * 1e3, 1),
+                                                           "TOPS": round(2.0 * M * N * K / ms / 1e9, 1)}
     torch.cuda.synchronize()
     return res
 

@@ -13,6 +13,9 @@
  *    low-rank branch added to the quantized product of the residual weight.
  *  - entrenar 0.7.8 src/quant/gguf_quant/q8_0.rs: GGUF Q8_0 blocks (32 values,
  *    f16 scale, 34 bytes), Q8_0::quantize and Q8_0::dequantize.
+ *  - OneTrainer wiki "Quantization", "Technical" entries of GGUF A8 int and
+ *    GGUF A8 float: GGUF weights re-quantized axis-wise (one scale per output
+ *    channel) to int8 or float8 e4m3, token-wise activations, 8-bit product.
  *
  * Shared rules
  *  - Absmax scale of a group (a row, a whole tensor, a 32-value block):
@@ -200,6 +203,34 @@ w8a8_status q8_0_quantize(const float *x, int64_t n, void *blocks, hipStream_t s
  * block i / 32 (an exact product).  blocks q8_0_nbytes(n) bytes; y f32 [n].
  */
 w8a8_status q8_0_dequantize(const void *blocks, int64_t n, float *y, hipStream_t stream);
+
+/* ----------------------------------------------------------------- GGUF A8 */
+
+/*
+ * GGUF A8 weight preparation (wiki "Quantization", GGUF A8 int / GGUF A8
+ * float, "Technical": weights re-quantized from GGUF to int8 / float8 e4m3
+ * axis-wise).  The GGUF weight is Q8_0: row n of W [N, K] is K / 32
+ * consecutive 34-byte blocks (as q8_0_quantize lays out N * K values), and
+ * its values are the exact dequantization f32(q) * f32(d).  Per row n:
+ *   w_scale[n] = absmax scale of the row's values (shared rules, QMAX of qtype)
+ *   wq[n, k]   = code of value k (shared rules)
+ *   blocks N * (K / 32) * 34 bytes; wq codes [N, K]; w_scale f32 [N].
+ * Shape rules: K % 32 == 0 and the block bytes below 2^31, else
+ * W8A8_ERR_SHAPE.  K == 0 gives the floor scale 1e-10 for every row.
+ */
+w8a8_status gguf_a8_requant_q8_0(w8a8_qtype qtype, const void *blocks, int64_t N, int64_t K, void *wq,
+                                 float *w_scale, hipStream_t stream);
+
+/*
+ * GGUF A8 linear: as w8a8_linear with one weight scale per output channel,
+ *   y[m, n] = bf16(acc[m, n] * x_scale[m] * w_scale[n] + bias[n])
+ *   xq codes [M, K] (w8a8_quant_act_rowwise), x_scale f32 [M]; wq codes
+ *   [N, K] and w_scale f32 [N] (gguf_a8_requant_q8_0); bias bf16 [N] or NULL;
+ *   y bf16 [M, N].  Shape rules as w8a8_linear.
+ */
+w8a8_status gguf_a8_linear(w8a8_qtype qtype, const void *xq, const float *x_scale, const void *wq,
+                           const float *w_scale, const uint16_t *bias, int64_t M, int64_t N, int64_t K, uint16_t *y,
+                           hipStream_t stream);
 
 #ifdef __cplusplus
 }

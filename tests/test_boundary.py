@@ -16,7 +16,7 @@ NULL = None
 
 def test_exports_match_header():
     names = w8.exported_names_in_header()
-    assert len(names) == 12
+    assert len(names) == 14
     for n in names:
         assert hasattr(lib, n), n
 
@@ -105,3 +105,22 @@ def test_binding_refuses_cpu_tensors():
         w8.w8a8_quant_act_rowwise(x)
     with pytest.raises(TypeError):
         w8.w8a8_quant_act_rowwise(x.float())
+
+
+def test_gguf_a8_rejects():
+    f = lib.gguf_a8_requant_q8_0
+    assert f(2, A, 8, 64, A, A, NULL) == INVALID                    # bad qtype
+    assert f(0, A, -1, 64, A, A, NULL) == INVALID
+    assert f(0, A, 8, 48, A, A, NULL) == SHAPE                      # K % 32
+    assert f(0, A, 1 << 20, 1 << 16, A, A, NULL) == SHAPE           # blocks >= 2 GB
+    assert f(0, NULL, 8, 64, A, A, NULL) == INVALID                 # null blocks
+    assert f(0, A, 8, 64, A, NULL, NULL) == INVALID                 # null scales
+    assert f(0, MIS, 8, 64, A, A, NULL) == ALIGN
+    assert f(1, A, 8, 64, A, MIS, NULL) == ALIGN
+    assert f(0, NULL, 0, 64, NULL, NULL, NULL) == OK                # N = 0: no-op
+    g = lib.gguf_a8_linear
+    assert g(0, A, A, A, A, NULL, 64, 64, 40, A, NULL) == SHAPE     # K % 16
+    assert g(0, A, A, A, NULL, NULL, 64, 64, 64, A, NULL) == INVALID
+    assert g(0, A, A, A, MIS, NULL, 64, 64, 64, A, NULL) == ALIGN
+    assert g(3, A, A, A, A, NULL, 64, 64, 64, A, NULL) == INVALID
+    assert g(0, NULL, NULL, NULL, NULL, NULL, 0, 64, 64, NULL, NULL) == OK

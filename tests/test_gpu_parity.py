@@ -326,6 +326,67 @@ def test_q8_0_full_config():
     assert_equal(y.cpu().numpy().view(np.uint32), oracle.q8_0_dequantize(ref, v.size).view(np.uint32), "dequant")
 
 
+# ------------------------------------------------------------ GGUF A8
+@pytest.mark.parametrize("qt", [INT8, FP8])
+@pytest.mark.parametrize("N,K", [(1, 32), (5, 64), (37, 160), (130, 2048), (9, 2080), (7, 4128), (300, 3072)])
+def test_gguf_a8_requant(qt, N, K):
+    _say(f"gguf a8 requant qt={qt} N={N} K={K}")
+    rng = np.random.default_rng(N * 7 + K)
+    blob = workloads.q8_0_weight_blocks(rng, N, K, zero_rows=1)
+    wq, s = W8.gguf_a8_requant_q8_0(torch.from_numpy(blob).cuda(), N, K, qtype=qt)
+    torch.cuda.synchronize()
+    ref_q, ref_s = oracle.gguf_a8_requant_q8_0(qt, blob, N, K)
+    assert_equal(s.cpu().numpy().view(np.uint32), ref_s.view(np.uint32), "scales")
+    assert_equal(bytes_host(wq), ref_q, "codes")
+
+
+def test_gguf_a8_requant_full():
+    _say("gguf a8 requant N=12288 K=3072 full")
+    d = workloads.gguf()
+    N, K = d["N"], d["K"]
+    blocks = torch.from_numpy(d["w_blocks"]).cuda()
+    for qt in (INT8, FP8):
+        wq, s = W8.gguf_a8_requant_q8_0(blocks, N, K, qtype=qt)
+        torch.cuda.synchronize()
+        ref_q, ref_s = oracle.gguf_a8_requant_q8_0(qt, d["w_blocks"], N, K)
+        assert_equal(s.cpu().numpy().view(np.uint32), ref_s.view(np.uint32), f"scales qt={qt}")
+        assert_equal(bytes_host(wq), ref_q, f"codes qt={qt}")
+
+
+def _gguf_chain(x_bits, blob, N, K, bias_bits, qt, rows=None):
+    """GPU: act-quant + requant + gguf_a8_linear; oracle: the same chain on `rows`."""
+    xq, sx = W8.w8a8_quant_act_rowwise(bf16_dev(x_bits), qtype=qt)
+    wq, sw = W8.gguf_a8_requant_q8_0(torch.from_numpy(blob).cuda(), N, K, qtype=qt)
+    b = None if bias_bits is None else bf16_dev(bias_bits)
+    y = W8.gguf_a8_linear(xq, sx, wq, sw, b)
+    torch.cuda.synchronize()
+    sel = np.arange(x_bits.shape[0]) if rows is None else rows
+    rxq, rsx = oracle.quant_act_rowwise(qt, x_bits[sel])
+    rwq, rsw = oracle.gguf_a8_requant_q8_0(qt, blob, N, K)
+    return bf16_host(y)[sel], oracle.linear_axiswise(qt, rxq, rsx, rwq, rsw, bias_bits)
+
+
+@pytest.mark.parametrize("qt", [INT8, FP8])
+@pytest.mark.parametrize("M,N,K", [(64, 256, 256), (1, 24, 32), (5, 200, 64), (257, 300, 288), (130, 520, 1056)])
+def test_gguf_a8_linear(qt, M, N, K):
+    _say(f"gguf a8 linear qt={qt} M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + 3 * N + K)
+    x = workloads.activations_bf16(rng, M, K, outliers=2)
+    blob = workloads.q8_0_weight_blocks(rng, N, K, zero_rows=1)
+    b = workloads.normal_bf16(rng, (N,), 0.02) if M % 2 else None
+    got, ref = _gguf_chain(x, blob, N, K, b, qt)
+    assert_bf16_close(got, ref, f"gguf a8 linear qt={qt}")
+
+
+def test_gguf_a8_linear_full_sampled():
+    _say("gguf a8 linear M=4096 N=12288 K=3072 sampled rows")
+    d = workloads.gguf()
+    rows = sample_rows(d["x"].shape[0], 6)
+    for qt in (INT8, FP8):
+        got, ref = _gguf_chain(d["x"], d["w_blocks"], d["N"], d["K"], d["bias"], qt, rows=rows)
+        assert_bf16_close(got, ref, f"gguf full qt={qt}")
+
+
 # ------------------------------------------------------------ determinism, graphs
 def test_determinism_and_graph_capture():
     _say("determinism + graph capture of act-quant + linear")

@@ -11,6 +11,8 @@ the current stream.  The functions carry the C names:
   w8a8_gemm_i32                 raw int32 accumulators (test export)
   svdq_linear                   residual 8-bit product + bf16 low-rank branch
   q8_0_quantize / q8_0_dequantize / q8_0_nbytes   GGUF Q8_0 blocks
+  gguf_a8_requant_q8_0          Q8_0 weight -> int8 / e4m3 codes, one scale per output channel
+  gguf_a8_linear                8-bit product with per-channel weight scales -> bf16
 
 Codes are torch.int8 (int8) or torch.float8_e4m3fn (e4m3); bf16 tensors are
 torch.bfloat16; scales are float32.  Output tensors may be passed in (`out=`)
@@ -56,6 +58,8 @@ def _load_library():
         "q8_0_nbytes": (ctypes.c_size_t, [I64]),
         "q8_0_quantize": (I, [P, I64, P, P]),
         "q8_0_dequantize": (I, [P, I64, P, P]),
+        "gguf_a8_requant_q8_0": (I, [I, P, I64, I64, P, P, P]),
+        "gguf_a8_linear": (I, [I, P, P, P, P, P, I64, I64, I64, P, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -250,3 +254,33 @@ def q8_0_dequantize(blocks, n, out=None):
     y = out if out is not None else torch.empty(max(n, 4), dtype=torch.float32, device=blocks.device)
     _check(_lib.q8_0_dequantize(_ptr(blocks), n, _ptr(y), _stream(blocks.device)))
     return y[:n]
+
+
+# ------------------------------------------------------------------- GGUF A8
+def gguf_a8_requant_q8_0(blocks, N, K, qtype=INT8, out=None, scale=None):
+    """Q8_0 weight [N, K] (uint8 blocks, row n = K / 32 blocks) -> (codes [N, K], scales f32 [N])."""
+    _need(blocks, torch.uint8, "blocks")
+    dev = blocks.device
+    wq = out if out is not None else torch.empty((N, K), dtype=_code_dtype(qtype), device=dev)
+    s = scale if scale is not None else torch.empty(max(N, 4), dtype=torch.float32, device=dev)
+    _check(_lib.gguf_a8_requant_q8_0(qtype, _ptr(blocks), N, K, _ptr(wq), _ptr(s), _stream(dev)))
+    return wq, s[:N]
+
+
+def gguf_a8_linear(xq, x_scale, wq, w_scale, bias=None, out=None):
+    """8-bit linear with per-output-channel weight scales w_scale f32 [N] -> bf16 [M, N]."""
+    qt = _qtype_of(xq)
+    if wq.dtype != xq.dtype:
+        raise TypeError("xq and wq must hold the same code type")
+    M, K = xq.shape
+    N = wq.shape[0]
+    if wq.shape[1] != K:
+        raise ValueError("xq and wq must share K")
+    _need(x_scale, torch.float32, "x_scale")
+    _need(w_scale, torch.float32, "w_scale")
+    if bias is not None:
+        _need(bias, torch.bfloat16, "bias")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    _check(_lib.gguf_a8_linear(qt, _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(bias), M, N, K, _ptr(y),
+                               _stream(xq.device)))
+    return y

@@ -392,13 +392,29 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         int el = lane;
         asm volatile("" : "+v"(el));
         const int erow = el & 31, ehalf = el >> 5;
+        constexpr bool kCol = EPI == kEpiColScale;
         float tm[4];
         uint2 bias2[4][4];
-        const float sw = p.sw[0];
+        v4f swc[kCol ? 4 : 1][4];  // per-channel weight scales of columns nb * 32 + 8 j + 4 half + i
+        const float sw = kCol ? 1.0f : p.sw[0];
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
             const int m = mw + mb * 32 + erow;
             tm[mb] = (kIn || m < M) ? p.sx[m] * sw : 0.0f;
+        }
+        if constexpr (kCol) {
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int n = nw + nb * 32 + 8 * j + 4 * ehalf;
+                    if (kIn || ((N & 3) == 0 && n < N)) {
+                        swc[nb][j] = *reinterpret_cast<const v4f *>(p.sw + n);
+                    } else {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) swc[nb][j][i] = n + i < N ? p.sw[n + i] : 0.0f;
+                    }
+                }
         }
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
@@ -426,6 +442,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
 #pragma unroll
                 for (int e = 0; e < 16; ++e) v[e] = (float)acc[nb][mb][e] * tm[mb];
                 if constexpr (EPI == kEpiLowRank) v = low_rank_add(p, v, nw + nb * 32, mw + mb * 32, erow, ehalf);
+                if constexpr (kCol) {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) v[e] *= swc[nb][e / 4][e % 4];
+                }
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const uint2 bb = bias2[nb][j];
@@ -562,11 +582,13 @@ w8a8_status gemm_launch(w8a8_qtype qtype, GemmEpilogue epi, const GemmArgs &a, h
     if (qtype == W8A8_INT8) {
         if (epi == kEpiI32) launch<W8A8_INT8, kEpiI32>(a, stream);
         else if (epi == kEpiBf16) launch<W8A8_INT8, kEpiBf16>(a, stream);
-        else launch<W8A8_INT8, kEpiLowRank>(a, stream);
+        else if (epi == kEpiLowRank) launch<W8A8_INT8, kEpiLowRank>(a, stream);
+        else launch<W8A8_INT8, kEpiColScale>(a, stream);
     } else {
         if (epi == kEpiI32) return W8A8_ERR_UNSUPPORTED;
         if (epi == kEpiBf16) launch<W8A8_FP8_E4M3, kEpiBf16>(a, stream);
-        else launch<W8A8_FP8_E4M3, kEpiLowRank>(a, stream);
+        else if (epi == kEpiLowRank) launch<W8A8_FP8_E4M3, kEpiLowRank>(a, stream);
+        else launch<W8A8_FP8_E4M3, kEpiColScale>(a, stream);
     }
     return launch_status();
 }
@@ -601,6 +623,28 @@ extern "C" w8a8_status w8a8_linear_backward_dx(w8a8_qtype qtype, const void *dyq
     // dX[M, K] = dYq[M, N] . Wq[N, K] = the NT product of dYq with Wq^T [K, N]
     // over the reduction length N.
     return w8a8_linear(qtype, dyq, dy_scale, wq_t, w_scale, nullptr, M, K, N, dx, stream);
+}
+
+extern "C" w8a8_status gguf_a8_linear(w8a8_qtype qtype, const void *xq, const float *x_scale, const void *wq,
+                                      const float *w_scale, const uint16_t *bias, int64_t M, int64_t N, int64_t K,
+                                      uint16_t *y, hipStream_t stream) {
+    using namespace w8a8;
+    if (!valid_qtype(qtype)) return W8A8_ERR_INVALID_ARG;
+    w8a8_status st = gemm_check(xq, wq, M, N, K, y);
+    if (st != W8A8_OK) return st;
+    if (M > 0 && N > 0 && (!x_scale || !w_scale)) return W8A8_ERR_INVALID_ARG;
+    if (!aligned16(x_scale) || !aligned16(w_scale) || !aligned16(bias)) return W8A8_ERR_ALIGN;
+    GemmArgs a = {};
+    a.xq = static_cast<const uint8_t *>(xq);
+    a.wq = static_cast<const uint8_t *>(wq);
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.sx = x_scale;
+    a.sw = w_scale;
+    a.bias = bias;
+    a.out = y;
+    return gemm_launch(qtype, kEpiColScale, a, stream);
 }
 
 extern "C" w8a8_status w8a8_gemm_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64_t K,

@@ -1,0 +1,157 @@
+// gguf_a8.hip -- weight preparation of the GGUF A8 quant types.
+//
+// OneTrainer wiki "Quantization", GGUF A8 int / GGUF A8 float ("Technical"):
+// the weight is loaded as the GGUF file stores it and re-quantized axis-wise
+// to int8 (float8 e4m3), one scale per output channel; the linear then runs
+// the 8-bit product on token-wise quantized activations, with the per-channel
+// weight scales applied in the product's epilogue (gguf_a8_linear, gemm.hip).
+// The GGUF format here is Q8_0 (entrenar q8_0.rs, struct Q8_0: 34-byte blocks
+// of an f16 scale d and 32 int8 codes); a weight row of K values is K / 32
+// consecutive blocks, and its values are the exact dequantization q * d.
+//
+// One wave per output row.  The row is streamed through the wave's LDS area
+// in chunks of 64 blocks (2176 bytes, fetched with 16-byte loads from the
+// 16-byte aligned address at or below the chunk), then 8 lanes take one block
+// (4 codes each).  Pass 1 finds the row absmax, pass 2 re-stages the row (an
+// L2 hit) and writes the codes: 8 blocks = 256 contiguous bytes per step.
+#include "internal.hpp"
+
+namespace w8a8 {
+namespace {
+
+constexpr int kThreads = 256;            // 4 waves, one row each
+constexpr int kChunkBlocks = 64;
+constexpr int kStageBytes = kChunkBlocks * 34 + 32;  // chunk + alignment slack, multiple of 16
+static_assert(kStageBytes % 16 == 0, "16-byte staging");
+
+template <int QT>
+__global__ __launch_bounds__(kThreads) void gguf_a8_requant_kernel(const uint8_t *__restrict__ blocks,
+                                                                   uint32_t total_bytes, int N, int K,
+                                                                   uint8_t *__restrict__ wq,
+                                                                   float *__restrict__ scale) {
+    __shared__ __attribute__((aligned(16))) uint8_t stage[kThreads / 64][kStageBytes];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    uint8_t *st = stage[wave];
+    const int nb = K / 32;
+    const uint32_t row_bytes = (uint32_t)nb * 34u;
+    // Whole tensor in one descriptor (total_bytes < 2^31 is checked on the
+    // host); loads past its end read zero.
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(blocks), (short)0, (int)total_bytes, kBufferRsrcWord3);
+    const float qmax = QT == W8A8_INT8 ? 127.0f : 448.0f;
+    const int blk_in_step = lane >> 3, part = lane & 7;  // 8 lanes per block, 4 codes each
+
+    // Stage blocks [c0, c0 + cb) of row n; returns the byte offset of block
+    // c0 within the staging area.
+    auto stage_chunk = [&](int n, int c0, int cb) -> int {
+        const uint32_t s0 = (uint32_t)n * row_bytes + (uint32_t)c0 * 34u;
+        const uint32_t a0 = s0 & ~15u;
+        const int off = (int)(s0 - a0);
+        const int nvec = (off + cb * 34 + 15) / 16;
+        for (int i = lane; i < nvec; i += 64) {
+            const uint32_t vo = a0 + 16u * i;
+            v4u v;
+            if (vo + 16u <= total_bytes) {
+                v = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0));
+            } else {
+                // the tensor's last 16 bytes run past its end: a wide load
+                // that crosses num_records reads zero as a whole, so take the
+                // remaining bytes one by one
+                uint8_t t[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) t[j] = __builtin_amdgcn_raw_buffer_load_b8(rs, vo + j, 0, 0);
+                v = __builtin_bit_cast(v4u, t);
+            }
+            *reinterpret_cast<v4u *>(st + 16 * i) = v;
+        }
+        return off;
+    };
+    // Values of this lane's 4 codes of block b of the staged chunk (0 past cb).
+    auto block_vals = [&](int off, int b, int cb, float *v) {
+        if (b < cb) {
+            const uint8_t *bp = st + off + b * 34;
+            const uint32_t dbits = *reinterpret_cast<const uint16_t *>(bp);
+            const uint32_t lo = *reinterpret_cast<const uint16_t *>(bp + 2 + 4 * part);
+            const uint32_t hi = *reinterpret_cast<const uint16_t *>(bp + 4 + 4 * part);
+            const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)dbits);
+            const uint32_t w = lo | (hi << 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = (float)(int8_t)(w >> (8 * i)) * d;  // exact in f32
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = 0.0f;
+        }
+    };
+
+    for (int n = blockIdx.x * (kThreads / 64) + wave; n < N; n += gridDim.x * (kThreads / 64)) {
+        // pass 1: row absmax (non-negative floats order like their bit patterns)
+        uint32_t amax_bits = 0;
+        for (int c0 = 0; c0 < nb; c0 += kChunkBlocks) {
+            const int cb = min(kChunkBlocks, nb - c0);
+            const int off = stage_chunk(n, c0, cb);
+            for (int b0 = 0; b0 < cb; b0 += 8) {
+                float v[4];
+                block_vals(off, b0 + blk_in_step, cb, v);
+                const float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+                amax_bits = max(amax_bits, __float_as_uint(a));
+            }
+        }
+        const float s = absmax_scale(__uint_as_float(wave_max_u32(amax_bits)), qmax);
+        if (lane == 0) scale[n] = s;
+        // pass 2: codes; the quotient is an IEEE division, as the oracle's
+        uint8_t *orow = wq + (size_t)n * K;
+        for (int c0 = 0; c0 < nb; c0 += kChunkBlocks) {
+            const int cb = min(kChunkBlocks, nb - c0);
+            const int off = stage_chunk(n, c0, cb);
+            for (int b0 = 0; b0 < cb; b0 += 8) {
+                const int b = b0 + blk_in_step;
+                float v[4];
+                block_vals(off, b, cb, v);
+                uint32_t word = 0;
+                if constexpr (QT == W8A8_INT8) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float q = __builtin_amdgcn_fmed3f(v[i] / s, -128.0f, 127.0f);
+                        word |= ((uint32_t)(int)__builtin_rintf(q) & 0xFFu) << (8 * i);
+                    }
+                } else {
+                    float q[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) q[i] = __builtin_amdgcn_fmed3f(v[i] / s, -448.0f, 448.0f);
+                    int pk = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+                    pk = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], pk, true);
+                    word = (uint32_t)pk;
+                }
+                if (b < cb) *reinterpret_cast<uint32_t *>(orow + (size_t)(c0 + b) * 32 + 4 * part) = word;
+            }
+        }
+    }
+}
+
+}  // namespace
+}  // namespace w8a8
+
+extern "C" w8a8_status gguf_a8_requant_q8_0(w8a8_qtype qtype, const void *blocks, int64_t N, int64_t K, void *wq,
+                                            float *w_scale, hipStream_t stream) {
+    using namespace w8a8;
+    if (!valid_qtype(qtype) || N < 0 || K < 0) return W8A8_ERR_INVALID_ARG;
+    if (K % 32 != 0 || K > (1 << 24) || N > (1 << 30)) return W8A8_ERR_SHAPE;
+    const int64_t total = N * (K / 32) * 34;
+    if (total >= ((int64_t)1 << 31)) return W8A8_ERR_SHAPE;
+    if (N == 0) return W8A8_OK;
+    // K == 0: no blocks, no codes; every row is all-zero and gets the floor scale
+    if (!w_scale || (K > 0 && (!blocks || !wq))) return W8A8_ERR_INVALID_ARG;
+    if (!aligned16(blocks) || !aligned16(wq) || !aligned16(w_scale)) return W8A8_ERR_ALIGN;
+    const int rows_per_wg = kThreads / 64;
+    int64_t grid = (N + rows_per_wg - 1) / rows_per_wg;
+    const int64_t cap = 8LL * device_cu_count();
+    if (grid > cap) grid = cap;
+    if (qtype == W8A8_INT8)
+        gguf_a8_requant_kernel<W8A8_INT8><<<(int)grid, kThreads, 0, stream>>>(
+            static_cast<const uint8_t *>(blocks), (uint32_t)total, (int)N, (int)K, static_cast<uint8_t *>(wq), w_scale);
+    else
+        gguf_a8_requant_kernel<W8A8_FP8_E4M3><<<(int)grid, kThreads, 0, stream>>>(
+            static_cast<const uint8_t *>(blocks), (uint32_t)total, (int)N, (int)K, static_cast<uint8_t *>(wq), w_scale);
+    return launch_status();
+}

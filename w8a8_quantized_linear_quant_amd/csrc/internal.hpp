@@ -11,6 +11,7 @@ enum GemmEpilogue {
     kEpiI32 = 0,      // raw int32 accumulators
     kEpiBf16 = 1,     // bf16(acc * sx[m] * sw + bias[n])
     kEpiLowRank = 2,  // bf16(acc * sx[m] * sw + u[m,:] . l2[n,:] + bias[n])
+    kEpiColScale = 3, // bf16(acc * sx[m] * sw[n] + bias[n]), one weight scale per output channel
 };
 
 struct GemmArgs {
@@ -18,7 +19,7 @@ struct GemmArgs {
     const uint8_t *wq;  // [N, K] codes
     int M, N, K;
     const float *sx;       // [M]
-    const float *sw;       // [1]
+    const float *sw;       // [1], or [N] for kEpiColScale
     const uint16_t *bias;  // [N] bf16 or null
     void *out;             // bf16 [M, N] or int32 [M, N]
     // low-rank branch: u split into bf16 hi/lo halves, [M, rp] each (zero

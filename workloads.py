@@ -19,6 +19,8 @@ models the pages mention; no dataset is involved):
   svdq   X [4096,3072] as dit, L1 [32,3072], L2 [12288,32] N(0,0.1),
          R [12288,3072] N(0,0.02), bias [12288] N(0,0.02)
   fp8    W [12288,3072] N(0,0.02), X [8192,3072] N(0,1), dY [8192,12288] N(0,1e-3)
+  gguf   W [12288,3072] as GGUF Q8_0 blocks (synthetic block contents, see
+         q8_0_weight_blocks), X [4096,3072] as dit, bias [12288] N(0,0.02)
 """
 import numpy as np
 import torch
@@ -104,3 +106,33 @@ def fp8_step(seed=0, M=8192, K=3072, N=12288):
 def random_rows(seed, M, K, std=1.0):
     """Generic N(0, std) bf16 matrix for edge-case shapes."""
     return normal_bf16(np.random.default_rng(seed), (M, K), std)
+
+
+def q8_0_weight_blocks(rng, N, K, zero_rows=0):
+    """A weight [N, K] as GGUF Q8_0 bytes (row n = K / 32 blocks of {f16 d, 32
+    int8 codes}), drawn directly rather than quantized: per block a scale
+    d = f16(0.02 * 3 / 127 * exp(N(0, 0.3))) and codes rint(N(0, 1) * 127 / 3)
+    clipped to [-127, 127], with one code of each block set to +-127 (as a
+    block's absmax element is).  The first `zero_rows` rows are all-zero codes.
+    Returns uint8 [N * K / 32 * 34]."""
+    assert K % 32 == 0
+    nb = N * K // 32
+    d = (0.02 * 3.0 / 127.0 * np.exp(rng.standard_normal(nb) * 0.3)).astype(np.float16)
+    q = np.clip(np.rint(rng.standard_normal((nb, 32)) * (127.0 / 3.0)), -127, 127)
+    pick = rng.integers(0, 32, nb)
+    q[np.arange(nb), pick] = np.where(rng.random(nb) < 0.5, -127.0, 127.0)
+    q = q.astype(np.int8)
+    if zero_rows:
+        q[: zero_rows * (K // 32)] = 0
+    out = np.empty((nb, 34), np.uint8)
+    out[:, :2] = d.view(np.uint8).reshape(nb, 2)
+    out[:, 2:] = q.view(np.uint8)
+    return out.ravel()
+
+
+def gguf(seed=0, M=4096, K=3072, N=12288):
+    rng = np.random.default_rng(seed)
+    x = activations_bf16(rng, M, K)
+    blocks = q8_0_weight_blocks(rng, N, K)
+    bias = normal_bf16(rng, (N,), 0.02)
+    return {"x": x, "w_blocks": blocks, "bias": bias, "N": N, "K": K}
