@@ -268,7 +268,13 @@ def other_rows(w8, torch, workloads, args):
     ms = _time_launches(lambda i: w8.w8a8_linear_backward_dx(dyq, sdy, wqt, sw, out=dx), iters, 3)
     res["fp8_bwd_dx_M8192_N12288_K3072"] = {"us": round(ms * 1e3, 1),
                                             "TFLOPS": round(2.0 * 8192 * N * K / ms / 1e9, 1)}
-    del wq, wqt, x, xq, y, dy, dyq, dx
+    # the int8 analogue of the train step's dX
+    wq8, wqt8, sw8 = w8.w8a8_quant_weight_tensorwise(_bf16(d["w"]), qtype=w8.INT8, transposed=True)
+    dyq8, sdy8 = w8.w8a8_quant_act_rowwise(dy, qtype=w8.INT8)
+    ms = _time_launches(lambda i: w8.w8a8_linear_backward_dx(dyq8, sdy8, wqt8, sw8, out=dx), iters, 3)
+    res["int8_bwd_dx_M8192_N12288_K3072"] = {"us": round(ms * 1e3, 1),
+                                             "TOPS": round(2.0 * 8192 * N * K / ms / 1e9, 1)}
+    del wq, wqt, x, xq, y, dy, dyq, dx, wq8, wqt8, dyq8
     # Q8_0
     v = torch.from_numpy(workloads.q8_0_vector()).cuda()
     n = v.numel()

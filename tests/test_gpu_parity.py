@@ -263,6 +263,43 @@ def test_fp8_step_forward_and_backward_sampled():
     assert_bf16_close(bf16_host(dx)[rows][:, kcols], ref_dx, "fp8 dX")
 
 
+@pytest.mark.parametrize("qt", [INT8, FP8])
+@pytest.mark.parametrize("M,N,K", [(64, 256, 256), (5, 48, 200), (257, 272, 296), (33, 1040, 64)])
+def test_backward_dx_ragged(qt, M, N, K):
+    """dX = dY . W through the transposed codes, ragged in every dimension
+    (dY [M, N] row-quantized, N the reduction length)."""
+    _say(f"backward dX qt={qt} M={M} N={N} K={K}")
+    rng = np.random.default_rng(M * 5 + N + K)
+    w = workloads.normal_bf16(rng, (N, K), 0.02)
+    dy = workloads.normal_bf16(rng, (M, N), 1e-3)
+    wq, wqt, sw = W8.w8a8_quant_weight_tensorwise(bf16_dev(w), qtype=qt, transposed=True)
+    dyq, sdy = W8.w8a8_quant_act_rowwise(bf16_dev(dy), qtype=qt)
+    dx = W8.w8a8_linear_backward_dx(dyq, sdy, wqt, sw)
+    torch.cuda.synchronize()
+    owq, owqt, osw = oracle.quant_weight_tensorwise(qt, w, transposed=True)
+    assert_equal(bytes_host(wqt), owqt, "transposed codes")
+    odyq, osdy = oracle.quant_act_rowwise(qt, dy)
+    assert_bf16_close(bf16_host(dx), oracle.linear_backward_dx(qt, odyq, osdy, owq, osw), f"dX qt={qt}")
+
+
+def test_int8_step_backward_sampled():
+    _say("int8 train step dX at M=8192 N=12288 K=3072 (sampled rows and columns)")
+    d = workloads.fp8_step()
+    w, dy = d["w"], d["dy"]
+    M, N = dy.shape
+    K = w.shape[1]
+    wq, wqt, sw = W8.w8a8_quant_weight_tensorwise(bf16_dev(w), qtype=INT8, transposed=True)
+    dyq, sdy = W8.w8a8_quant_act_rowwise(bf16_dev(dy), qtype=INT8)
+    dx = W8.w8a8_linear_backward_dx(dyq, sdy, wqt, sw)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, 4)
+    kcols = np.unique(np.concatenate([np.arange(0, K, 29), [K - 1]]))
+    owq, _, osw = oracle.quant_weight_tensorwise(INT8, w)
+    odyq, osdy = oracle.quant_act_rowwise(INT8, dy[rows])
+    ref_dx = oracle.linear_backward_dx(INT8, odyq, osdy, np.ascontiguousarray(owq[:, kcols]), osw)
+    assert_bf16_close(bf16_host(dx)[rows][:, kcols], ref_dx, "int8 dX")
+
+
 # ------------------------------------------------------------ SVDQuant
 @pytest.mark.parametrize("qt", [INT8, FP8])
 @pytest.mark.parametrize("M,K,N,r", [(64, 256, 256, 32), (37, 96, 130, 5), (130, 512, 520, 16), (16, 64, 48, 64)])
