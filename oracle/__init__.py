@@ -8,6 +8,8 @@ file for the passages of the pages each function follows.
 
 Arrays: bf16 and f16 travel as uint16 bit patterns, e4m3 codes as uint8, int8
 codes as int8 (viewed as uint8 where the C side takes bytes).
+
+oracle.svd_prep holds the SVDQuant weight preparation (numpy, float64).
 """
 import ctypes
 import os
