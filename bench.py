@@ -302,6 +302,21 @@ def other_rows(w8, torch, workloads, args):
         ms = _time_launches(lambda i: w8.gguf_a8_linear(xq, sx, wq, sw, bb, out=y), iters, 3)
         res[f"gguf_a8_linear_{tag}_M4096_K3072_N12288"] = {"us": round(ms * 1e3, 1),
                                                            "TOPS": round(2.0 * M * N * K / ms / 1e9, 1)}
+    # SVDQuant weight preparation of the SVDQuant workload's weight, r = 32, 2 power iterations
+    d = workloads.svdq()
+    l2p, l1p, rp = (torch.from_numpy(workloads.bf16_bits_to_f32(d[k])).double() for k in ("l2", "l1", "r"))
+    wsv = (l2p @ l1p + rp).float().to(torch.bfloat16).cuda()
+    del l2p, l1p, rp
+    s = w8.svdq_prepare_subspace(32)
+    om = _bf16(workloads.normal_bf16(np.random.default_rng(11), (s, K), 1.0))
+    l1o = torch.empty((32, K), dtype=torch.bfloat16, device="cuda")
+    l2o = torch.empty((N, 32), dtype=torch.bfloat16, device="cuda")
+    ro = torch.empty((N, K), dtype=torch.bfloat16, device="cuda")
+    so = torch.empty(32, dtype=torch.float32, device="cuda")
+    ws = torch.empty(w8.svdq_prepare_workspace_bytes(N, K, 32), dtype=torch.uint8, device="cuda")
+    ms = _time_launches(lambda i: w8.svdq_prepare(wsv, 32, om, iters=2, l1=l1o, l2=l2o, residual=ro, sigma=so,
+                                                  workspace=ws), 5, 1)
+    res["svdq_prepare_N12288_K3072_r32_iters2"] = {"us": round(ms * 1e3, 1)}
     torch.cuda.synchronize()
     return res
 

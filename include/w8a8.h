@@ -183,6 +183,30 @@ w8a8_status svdq_linear(w8a8_qtype qtype, const uint16_t *x, int64_t M, int64_t 
                         const uint16_t *bias, int64_t N, uint16_t *y, void *xq_out,
                         float *x_scale_out, void *workspace, hipStream_t stream);
 
+/*
+ * SVDQuant weight preparation (OneTrainer PR #1034 "SVDQuant"; wiki SVDQuant:
+ * bf16 factors, rank 16-32): the rank-r truncated SVD of W, W_r = U_r S_r V_r^T,
+ * stored balanced in the layout svdq_linear takes,
+ *   l2 = bf16(U_r S_r^(1/2))  [N, r],   l1 = bf16(S_r^(1/2) V_r^T)  [r, K],
+ * and the residual R = bf16(W - l2 . l1) [N, K] (to be quantized with
+ * w8a8_quant_weight_tensorwise); sigma f32 [r] = the singular values found.
+ * The SVD is computed by randomized subspace iteration (Halko, Martinsson,
+ * Tropp 2011) with `iters` power iterations (0..16) in a subspace of
+ * s = svdq_prepare_subspace(r) columns, started from the caller's Gaussian
+ * test matrix omega bf16 [s, K] (the method's random draw, an input).  The
+ * result approximates the exact truncated SVD; the error shrinks with iters
+ * and with the gap between sigma_r and sigma_{s+1}.
+ *   w bf16 [N, K]; workspace svdq_prepare_workspace_bytes(N, K, r) bytes
+ *   (about 2 N K + 8 (N + K) s bytes).
+ * Shape rules: 1 <= r <= 64, r <= N, r <= K, N % 8 == K % 8 == 0,
+ * N * K <= 2^31; else W8A8_ERR_INVALID_ARG (r, iters) or W8A8_ERR_SHAPE.
+ */
+int64_t svdq_prepare_subspace(int64_t r);
+size_t svdq_prepare_workspace_bytes(int64_t N, int64_t K, int64_t r);
+w8a8_status svdq_prepare(const uint16_t *w, int64_t N, int64_t K, int64_t r, const uint16_t *omega, int iters,
+                         uint16_t *l1, uint16_t *l2, uint16_t *residual, float *sigma, void *workspace,
+                         hipStream_t stream);
+
 /* -------------------------------------------------------------------- Q8_0 */
 
 /* Size in bytes of n values in GGUF Q8_0 blocks: 34 * ceil(n / 32) (struct

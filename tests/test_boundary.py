@@ -16,7 +16,7 @@ NULL = None
 
 def test_exports_match_header():
     names = w8.exported_names_in_header()
-    assert len(names) == 14
+    assert len(names) == 17
     for n in names:
         assert hasattr(lib, n), n
 
@@ -124,3 +124,22 @@ def test_gguf_a8_rejects():
     assert g(0, A, A, A, MIS, NULL, 64, 64, 64, A, NULL) == ALIGN
     assert g(3, A, A, A, A, NULL, 64, 64, 64, A, NULL) == INVALID
     assert g(0, NULL, NULL, NULL, NULL, NULL, 0, 64, 64, NULL, NULL) == OK
+
+
+def test_svdq_prepare_rejects_and_sizes():
+    assert [lib.svdq_prepare_subspace(r) for r in (1, 16, 32, 48, 49, 64)] == [32, 32, 48, 64, 64, 64]
+    assert lib.svdq_prepare_subspace(0) == 0 and lib.svdq_prepare_subspace(65) == 0
+    assert lib.svdq_prepare_workspace_bytes(12288, 3072, 32) >= 2 * 12288 * 3072
+    assert lib.svdq_prepare_workspace_bytes(8, 8, 0) == 0
+    f = lib.svdq_prepare
+
+    def args(N=64, K=64, r=8, it=2, w=A, om=A):
+        return (w, N, K, r, om, it, A, A, A, A, A, NULL)
+
+    assert f(*args(r=0)) == INVALID
+    assert f(*args(r=65)) == INVALID
+    assert f(*args(it=-1)) == INVALID
+    assert f(*args(N=60)) == SHAPE                                  # N % 8
+    assert f(*args(K=16, r=24)) == SHAPE                            # r > K
+    assert f(*args(w=NULL)) == INVALID
+    assert f(*args(om=MIS)) == ALIGN

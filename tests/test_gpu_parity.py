@@ -424,6 +424,85 @@ def test_gguf_a8_linear_full_sampled():
         assert_bf16_close(got, ref, f"gguf full qt={qt}")
 
 
+# ------------------------------------------------------------ SVDQuant preparation
+def _planted_bf16(rng, N, K, sigma):
+    u, _ = np.linalg.qr(rng.standard_normal((N, len(sigma))))
+    v, _ = np.linalg.qr(rng.standard_normal((K, len(sigma))))
+    return oracle.f64_to_bf16((u * sigma[None, :]) @ v.T)
+
+
+def _svd_prep_check(w_bits, r, iters, seed, sig_tol, lr_tol, energy_tol, what):
+    from oracle import svd_prep
+    N, K = w_bits.shape
+    s = W8.svdq_prepare_subspace(r)
+    omega = workloads.normal_bf16(np.random.default_rng(seed), (s, K), 1.0)
+    l1, l2, res, sg = W8.svdq_prepare(bf16_dev(w_bits), r, bf16_dev(omega), iters=iters)
+    torch.cuda.synchronize()
+    l1_g, l2_g, res_g, sg_g = bf16_host(l1), bf16_host(l2), bf16_host(res), sg.cpu().numpy().astype(np.float64)
+    sig_o, l1_o, l2_o, res_o = svd_prep.svdq_prepare(w_bits, r)
+    # singular values, relative to the largest
+    assert np.max(np.abs(sg_g - sig_o)) <= sig_tol * max(sig_o[0], 1e-30), (what, sg_g[:4], sig_o[:4])
+    # the low-rank part (sign- and basis-invariant)
+    p_g, p_o = svd_prep.low_rank(l2_g, l1_g), svd_prep.low_rank(l2_o, l1_o)
+    assert np.linalg.norm(p_g - p_o) <= lr_tol * max(np.linalg.norm(p_o), 1e-30), what
+    # the residual is W minus the stored factors' product, element by element
+    # (f32 sums on the GPU, double in the oracle: one bf16 rounding apart)
+    ref = svd_prep.residual(w_bits, l2_g, l1_g)
+    got_v, ref_v = oracle.bf16_to_f64(res_g), oracle.bf16_to_f64(ref)
+    slack = 2.0 ** -7 * np.abs(ref_v) + 2.0 ** -20 * np.max(np.abs(p_g)) + 1e-30
+    assert np.all(np.abs(got_v - ref_v) <= slack), what
+    # and its energy is close to the optimum (Eckart-Young)
+    e_g, e_o = np.sum(got_v ** 2), np.sum(oracle.bf16_to_f64(res_o) ** 2)
+    assert e_g <= e_o * (1.0 + energy_tol) + 1e-30, (what, e_g, e_o)
+    return sg_g, sig_o
+
+
+# Tolerances from the subspace-iteration error at this spectrum (sigma_i =
+# 4 * 2^(-i/4)): with power iterations the factors are limited by their bf16
+# rounding (~2e-4 of the low-rank part); without, or with no oversampling
+# (r = 64 = s), by the captured subspace.
+@pytest.mark.parametrize("r,iters,sig_tol,lr_tol,e_tol", [(16, 2, 1e-5, 1e-3, 1e-4), (32, 2, 1e-5, 1e-3, 1e-3),
+                                                          (8, 0, 1e-3, 5e-2, 5e-2), (48, 1, 2e-4, 2e-3, 1e-2),
+                                                          (64, 2, 2e-4, 3e-3, 2e-2)])
+def test_svdq_prepare_planted(r, iters, sig_tol, lr_tol, e_tol):
+    _say(f"svdq_prepare planted spectrum r={r} iters={iters}")
+    rng = np.random.default_rng(r + 100 * iters)
+    N, K = 512, 384
+    sigma = 4.0 * 2.0 ** (-np.arange(128) / 4.0)
+    w = _planted_bf16(rng, N, K, sigma)
+    _svd_prep_check(w, r, iters, r + 7, sig_tol=sig_tol, lr_tol=lr_tol, energy_tol=e_tol, what=f"r={r}")
+
+
+@pytest.mark.parametrize("N,K", [(8, 8), (24, 640), (1000, 72)])
+def test_svdq_prepare_shapes(N, K):
+    _say(f"svdq_prepare shape N={N} K={K}")
+    rng = np.random.default_rng(N + K)
+    sigma = 2.0 ** -np.arange(min(N, K), dtype=np.float64)
+    w = _planted_bf16(rng, N, K, sigma)
+    r = min(4, N, K)
+    _svd_prep_check(w, r, 2, 3, sig_tol=1e-4, lr_tol=1e-2, energy_tol=1e-2, what=f"{N}x{K}")
+
+
+def test_svdq_prepare_zero():
+    _say("svdq_prepare zero matrix")
+    w = np.zeros((64, 128), np.uint16)
+    omega = workloads.normal_bf16(np.random.default_rng(0), (W8.svdq_prepare_subspace(16), 128), 1.0)
+    l1, l2, res, sg = W8.svdq_prepare(bf16_dev(w), 16, bf16_dev(omega))
+    torch.cuda.synchronize()
+    assert not bf16_host(l1).any() and not bf16_host(l2).any() and not bf16_host(res).any()
+    assert not sg.cpu().numpy().any()
+
+
+def test_svdq_prepare_full_workload():
+    """The SVDQuant workload's weight W = bf16(L2 L1 + R) at 12288 x 3072,
+    r = 32: the preparation recovers the planted low-rank part."""
+    _say("svdq_prepare N=12288 K=3072 r=32 (planted: L2 L1 + R)")
+    d = workloads.svdq()
+    l2p, l1p, rp = (oracle.bf16_to_f64(d[k]) for k in ("l2", "l1", "r"))
+    w = oracle.f64_to_bf16(l2p @ l1p + rp)
+    _svd_prep_check(w, 32, 2, 11, sig_tol=1e-5, lr_tol=2e-3, energy_tol=1e-4, what="full")
+
+
 # ------------------------------------------------------------ determinism, graphs
 def test_determinism_and_graph_capture():
     _say("determinism + graph capture of act-quant + linear")

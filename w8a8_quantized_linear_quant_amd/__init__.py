@@ -10,6 +10,7 @@ the current stream.  The functions carry the C names:
   w8a8_linear_backward_dx       dX = dY . W from quantized dY and W^T codes
   w8a8_gemm_i32                 raw int32 accumulators (test export)
   svdq_linear                   residual 8-bit product + bf16 low-rank branch
+  svdq_prepare                  W -> bf16 low-rank pair (truncated SVD) + bf16 residual
   q8_0_quantize / q8_0_dequantize / q8_0_nbytes   GGUF Q8_0 blocks
   gguf_a8_requant_q8_0          Q8_0 weight -> int8 / e4m3 codes, one scale per output channel
   gguf_a8_linear                8-bit product with per-channel weight scales -> bf16
@@ -60,6 +61,9 @@ def _load_library():
         "q8_0_dequantize": (I, [P, I64, P, P]),
         "gguf_a8_requant_q8_0": (I, [I, P, I64, I64, P, P, P]),
         "gguf_a8_linear": (I, [I, P, P, P, P, P, I64, I64, I64, P, P]),
+        "svdq_prepare_subspace": (I64, [I64]),
+        "svdq_prepare_workspace_bytes": (ctypes.c_size_t, [I64, I64, I64]),
+        "svdq_prepare": (I, [P, I64, I64, I64, P, I, P, P, P, P, P, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -231,6 +235,35 @@ def svdq_linear(x, rq, r_scale, l1, l2, bias=None, out=None, xq_out=None, x_scal
                             _ptr(l2.contiguous()), r, _ptr(bias), N, _ptr(y), _ptr(xq), _ptr(sx), _ptr(ws),
                             _stream(dev)))
     return y, xq, sx
+
+
+def svdq_prepare_subspace(r):
+    return int(_lib.svdq_prepare_subspace(r))
+
+
+def svdq_prepare_workspace_bytes(N, K, r):
+    return int(_lib.svdq_prepare_workspace_bytes(N, K, r))
+
+
+def svdq_prepare(w, r, omega, iters=2, l1=None, l2=None, residual=None, sigma=None, workspace=None):
+    """w bf16 [N, K]; omega bf16 [svdq_prepare_subspace(r), K] (Gaussian).
+    Returns (l1 bf16 [r, K], l2 bf16 [N, r], residual bf16 [N, K], sigma f32 [r])."""
+    _need(w, torch.bfloat16, "w")
+    _need(omega, torch.bfloat16, "omega")
+    w = w.contiguous()
+    N, K = w.shape
+    if tuple(omega.shape) != (svdq_prepare_subspace(r), K):
+        raise ValueError("omega must be [svdq_prepare_subspace(r), K]")
+    dev = w.device
+    l1 = l1 if l1 is not None else torch.empty((r, K), dtype=torch.bfloat16, device=dev)
+    l2 = l2 if l2 is not None else torch.empty((N, r), dtype=torch.bfloat16, device=dev)
+    res = residual if residual is not None else torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    sg = sigma if sigma is not None else torch.empty(max(r, 4), dtype=torch.float32, device=dev)
+    ws = workspace if workspace is not None else torch.empty(max(svdq_prepare_workspace_bytes(N, K, r), 16),
+                                                             dtype=torch.uint8, device=dev)
+    _check(_lib.svdq_prepare(_ptr(w), N, K, r, _ptr(omega.contiguous()), iters, _ptr(l1), _ptr(l2), _ptr(res),
+                             _ptr(sg), _ptr(ws), _stream(dev)))
+    return l1, l2, res, sg[:r]
 
 
 # ---------------------------------------------------------------------- Q8_0
