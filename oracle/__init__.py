@@ -59,6 +59,9 @@ def _load():
         "orc_convert_array": (I, [I, P, I64, P]),
         "orc_gguf_a8_requant_q8_0": (I, [I, P, I64, I64, P, P, P]),
         "orc_linear_axiswise": (I, [I, P, P, P, P, P, I64, I64, I64, P]),
+        "orc_hadamard_block": (I64, [I64]),
+        "orc_hadamard_rows_f32": (I, [P, I64, I64, I64, P]),
+        "orc_quant_act_rowwise_hadamard": (I, [I, P, I64, I64, I64, P, I64, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -283,3 +286,35 @@ def linear_axiswise(qtype, xq, sx, wq, sw, bias=None):
     _check(_load().orc_linear_axiswise(qtype, _p(xq), _p(sx), _p(wq), _p(sw), _p(b), M, N, K, _p(y)),
            "linear_axiswise")
     return y
+
+
+# ---------------------------------------------------------------- Hadamard rotation
+def hadamard_block(K):
+    return int(_load().orc_hadamard_block(int(K)))
+
+
+def hadamard_rows_f32(x_bf16):
+    """Rotated rows (block-diagonal normalized Walsh-Hadamard along K), f32 [M, K]."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    out = np.empty((M, K), np.float32)
+    _check(_load().orc_hadamard_rows_f32(_p(x), M, K, K, _p(out)), "hadamard_rows_f32")
+    return out
+
+
+def hadamard_rotate_bf16(x_bf16):
+    """Rotated rows rounded to bf16 (the weight-side rotation) -> uint16 [M, K]."""
+    return f32_to_bf16(hadamard_rows_f32(x_bf16))
+
+
+def quant_act_rowwise_hadamard(qtype, x_bf16, ldq=None):
+    """Row-wise quantization of the rotated rows.  Returns (codes [M, ldq], scales f32 [M])."""
+    x = _c(x_bf16, np.uint16)
+    M, K = x.shape
+    ldq = K if ldq is None else ldq
+    q = np.empty((M, ldq), np.uint8)
+    s = np.empty(M, np.float32)
+    w = np.empty(max(K, 1), np.float32)
+    _check(_load().orc_quant_act_rowwise_hadamard(qtype, _p(x), M, K, K, _p(q), ldq, _p(s), _p(w)),
+           "quant_act_rowwise_hadamard")
+    return q, s

@@ -431,6 +431,69 @@ int orc_linear_axiswise(int qtype, const uint8_t *xq, const float *sx, const uin
 }
 
 /* ------------------------------------------------------------------------- */
+/* Hadamard rotation before quantization (diffusers "SDNQ" overview: "Hadamard */
+/* rotation"; named only there).  Definition used, from outside the pages: the  */
+/* input dimension K is split into blocks of b = min(1024, largest power of two */
+/* dividing K) and each block is multiplied by the normalized Sylvester         */
+/* Walsh-Hadamard matrix H_b / sqrt(b) (orthogonal and symmetric, so rotating   */
+/* both X and W leaves X W^T unchanged).  It is evaluated as the fast transform */
+/* in f32: stages h = 1, 2, 4, ..., b/2, each replacing the pair (x[i],         */
+/* x[i + h]) (i with bit h clear) by (x[i] + x[i + h], x[i] - x[i + h]), then   */
+/* every value times c = f32(1 / sqrt(b)); one rounding per operation.         */
+/* ------------------------------------------------------------------------- */
+int64_t orc_hadamard_block(int64_t K) {
+    if (K <= 0) return 0;
+    int64_t b = 1;
+    while (K % (b * 2) == 0 && b * 2 <= 1024) b *= 2;
+    return b;
+}
+
+/* out f32 [M, K] = rotated rows of the bf16 x [M, ldx] (first K columns). */
+int orc_hadamard_rows_f32(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, float *out) {
+    if (M < 0 || K < 0 || ldx < K) return ORC_ERR;
+    const int64_t b = orc_hadamard_block(K);
+    const float c = (float)(1.0 / sqrt((double)b));
+    for (int64_t m = 0; m < M; ++m) {
+        float *o = out + m * K;
+        for (int64_t k = 0; k < K; ++k) o[k] = (float)orc_bf16_to_f64(x[m * ldx + k]);
+        for (int64_t blk = 0; blk < K; blk += b) {
+            float *v = o + blk;
+            for (int64_t h = 1; h < b; h *= 2)
+                for (int64_t i = 0; i < b; ++i)
+                    if ((i & h) == 0) {
+                        const float a = v[i], d = v[i + h];
+                        v[i] = a + d;
+                        v[i + h] = a - d;
+                    }
+            for (int64_t i = 0; i < b; ++i) v[i] = v[i] * c;
+        }
+    }
+    return ORC_OK;
+}
+
+/* Row-wise quantization of the rotated rows (the shared absmax rule on the f32
+ * rotated values).  work: f32 [K]. */
+int orc_quant_act_rowwise_hadamard(int qtype, const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                                   uint8_t *q, int64_t ldq, float *scale, float *work) {
+    if ((qtype != 0 && qtype != 1) || M < 0 || K < 0 || ldx < K || ldq < K) return ORC_ERR;
+    const float qmax = qtype == 0 ? 127.0f : 448.0f;
+    for (int64_t m = 0; m < M; ++m) {
+        if (orc_hadamard_rows_f32(x + m * ldx, 1, K, K, work) != ORC_OK) return ORC_ERR;
+        float amax = 0.0f;
+        for (int64_t k = 0; k < K; ++k) {
+            float a = fabsf(work[k]);
+            if (a > amax) amax = a;
+        }
+        float s = orc_absmax_scale(amax, qmax);
+        scale[m] = s;
+        for (int64_t k = 0; k < K; ++k)
+            q[m * ldq + k] = qtype == 0 ? (uint8_t)orc_code_int8(work[k], s) : orc_code_e4m3(work[k], s);
+        for (int64_t k = K; k < ldq; ++k) q[m * ldq + k] = 0;
+    }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------- */
 /* Array forms of the scalar conversions above (same arithmetic, one call).    */
 /* kind: 0 f32->bf16, 1 f64->bf16, 2 f32->f16, 3 f64->f16, 4 f32->e4m3,        */
 /*       5 f64->e4m3, 6 bf16->f64, 7 f16->f64, 8 e4m3->f64.                     */
