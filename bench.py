@@ -302,6 +302,15 @@ def other_rows(w8, torch, workloads, args):
         ms = _time_launches(lambda i: w8.gguf_a8_linear(xq, sx, wq, sw, bb, out=y), iters, 3)
         res[f"gguf_a8_linear_{tag}_M4096_K3072_N12288"] = {"us": round(ms * 1e3, 1),
                                                            "TOPS": round(2.0 * M * N * K / ms / 1e9, 1)}
+    # act-quant of the headline X with the Hadamard rotation fused (K = 3072: three 1024-blocks)
+    d = workloads.svdq()
+    xh = _bf16(d["x"])
+    xqh = torch.empty((M, K), dtype=torch.int8, device="cuda")
+    sxh = torch.empty(M, dtype=torch.float32, device="cuda")
+    ms = _time_launches(lambda i: w8.w8a8_quant_act_rowwise_hadamard(xh, out=xqh, scale=sxh), iters, 3)
+    res["act_quant_hadamard_int8_X4096x3072"] = {"us": round(ms * 1e3, 1),
+                                                 "GB/s": round((3.0 * M * K + 4 * M) / ms / 1e6, 1)}
+    del xh, xqh
     # SVDQuant weight preparation of the SVDQuant workload's weight, r = 32, 2 power iterations
     d = workloads.svdq()
     l2p, l1p, rp = (torch.from_numpy(workloads.bf16_bits_to_f32(d[k])).double() for k in ("l2", "l1", "r"))

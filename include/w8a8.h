@@ -228,6 +228,28 @@ w8a8_status q8_0_quantize(const float *x, int64_t n, void *blocks, hipStream_t s
  */
 w8a8_status q8_0_dequantize(const void *blocks, int64_t n, float *y, hipStream_t stream);
 
+/* ---------------------------------------------------------------- Hadamard */
+
+/*
+ * Hadamard rotation before quantization (diffusers "SDNQ" overview names it;
+ * the definition is the standard one, not the pages'): K is cut into blocks of
+ * b = min(1024, largest power of two dividing K) and each block of a row is
+ * multiplied by the normalized Sylvester Walsh-Hadamard matrix H_b / sqrt(b),
+ * which is orthogonal and symmetric: rotating X and W alike leaves X W^T
+ * unchanged.  Evaluated as the fast transform in f32 (stages h = 1, 2, ...,
+ * b/2: (x[i], x[i+h]) -> (x[i] + x[i+h], x[i] - x[i+h]) for bit h of i clear),
+ * then times c = f32(1 / sqrt(b)); bit-reproducible.
+ *
+ * w8a8_quant_act_rowwise_hadamard: as w8a8_quant_act_rowwise, on the rotated
+ * rows (the shared absmax rule on the f32 rotated values).  K % 16 == 0.
+ * w8a8_hadamard_rotate: out bf16 [M, ldo] = the rotated rows of x rounded to
+ * bf16 (for the weight, which is then quantized as any weight).  K % 16 == 0.
+ */
+w8a8_status w8a8_quant_act_rowwise_hadamard(w8a8_qtype qtype, const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
+                                            void *xq, int64_t ldq, float *x_scale, hipStream_t stream);
+w8a8_status w8a8_hadamard_rotate(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, uint16_t *out, int64_t ldo,
+                                 hipStream_t stream);
+
 /* ----------------------------------------------------------------- GGUF A8 */
 
 /*

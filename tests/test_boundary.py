@@ -16,7 +16,7 @@ NULL = None
 
 def test_exports_match_header():
     names = w8.exported_names_in_header()
-    assert len(names) == 17
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
 
@@ -143,3 +143,16 @@ def test_svdq_prepare_rejects_and_sizes():
     assert f(*args(K=16, r=24)) == SHAPE                            # r > K
     assert f(*args(w=NULL)) == INVALID
     assert f(*args(om=MIS)) == ALIGN
+
+
+def test_hadamard_rejects():
+    f = lib.w8a8_quant_act_rowwise_hadamard
+    assert f(0, A, 4, 40, 40, A, 48, A, NULL) == SHAPE              # K % 16
+    assert f(2, A, 4, 64, 64, A, 64, A, NULL) == INVALID
+    assert f(0, MIS, 4, 64, 64, A, 64, A, NULL) == ALIGN
+    assert f(0, NULL, 0, 64, 64, NULL, 64, NULL, NULL) == OK         # M = 0
+    g = lib.w8a8_hadamard_rotate
+    assert g(A, 4, 40, 40, A, 40, NULL) == SHAPE
+    assert g(A, -1, 64, 64, A, 64, NULL) == INVALID
+    assert g(A, 4, 64, 64, MIS, 64, NULL) == ALIGN
+    assert g(NULL, 0, 64, 64, NULL, 64, NULL) == OK

@@ -503,6 +503,52 @@ def test_svdq_prepare_full_workload():
     _svd_prep_check(w, 32, 2, 11, sig_tol=1e-5, lr_tol=2e-3, energy_tol=1e-4, what="full")
 
 
+# ------------------------------------------------------------ Hadamard rotation
+@pytest.mark.parametrize("qt", [INT8, FP8])
+@pytest.mark.parametrize("M,K,ldq", [(5, 16, None), (37, 48, 64), (64, 96, None), (130, 1024, 1040), (9, 2048, None),
+                                     (300, 3072, None), (17, 4096, None), (8, 1040, None), (3, 12288, None)])
+def test_hadamard_act_quant(qt, M, K, ldq):
+    _say(f"hadamard act-quant qt={qt} M={M} K={K} ldq={ldq}")
+    rng = np.random.default_rng(M * 31 + K)
+    x = workloads.activations_bf16(rng, M, K, outliers=min(4, K // 16))
+    if M > 4:
+        x[1] = 0                                            # an all-zero row
+    xq, sx = W8.w8a8_quant_act_rowwise_hadamard(bf16_dev(x), qtype=qt, ldq=ldq)
+    torch.cuda.synchronize()
+    got_q = bytes_host(xq)
+    ref_q, ref_s = oracle.quant_act_rowwise_hadamard(qt, x, ldq=got_q.shape[1])
+    assert_equal(sx.cpu().numpy().view(np.uint32), ref_s.view(np.uint32), "scales")
+    assert_equal(got_q, ref_q, "codes")
+
+
+@pytest.mark.parametrize("M,K", [(7, 16), (33, 96), (64, 1024), (20, 3072), (5, 12288)])
+def test_hadamard_rotate(M, K):
+    _say(f"hadamard rotate M={M} K={K}")
+    x = workloads.normal_bf16(np.random.default_rng(K + M), (M, K), 0.02)
+    y = W8.w8a8_hadamard_rotate(bf16_dev(x))
+    torch.cuda.synchronize()
+    assert_equal(bf16_host(y), oracle.hadamard_rotate_bf16(x), "rotated bf16")
+
+
+def test_hadamard_linear_full_sampled():
+    """Rotated act-quant of X [4096, 3072] + rotated, tensor-wise quantized W
+    [12288, 3072] + the int8 linear, against the oracle chain on sampled rows."""
+    _say("hadamard linear M=4096 K=3072 N=12288 sampled rows")
+    d = workloads.dit(M=4096, N1=256)
+    x, w, b = d["x"], d["w2"], d["b2"]
+    xq, sx = W8.w8a8_quant_act_rowwise_hadamard(bf16_dev(x))
+    wr = W8.w8a8_hadamard_rotate(bf16_dev(w))
+    wq, _, sw = W8.w8a8_quant_weight_tensorwise(wr)
+    y = W8.w8a8_linear(xq, sx, wq, sw, bf16_dev(b))
+    torch.cuda.synchronize()
+    rows = sample_rows(x.shape[0], 6)
+    oxq, osx = oracle.quant_act_rowwise_hadamard(INT8, x[rows])
+    owr = oracle.hadamard_rotate_bf16(w)
+    assert_equal(bf16_host(wr), owr, "rotated weight")
+    owq, _, osw = oracle.quant_weight_tensorwise(INT8, owr)
+    assert_bf16_close(bf16_host(y)[rows], oracle.linear(INT8, oxq, osx, owq, osw, b), "hadamard linear")
+
+
 # ------------------------------------------------------------ determinism, graphs
 def test_determinism_and_graph_capture():
     _say("determinism + graph capture of act-quant + linear")

@@ -6,6 +6,8 @@ the current stream.  The functions carry the C names:
 
   w8a8_quant_weight_tensorwise  tensor-wise int8 / e4m3 weight quantization
   w8a8_quant_act_rowwise        row-wise (token-wise) activation quantization
+  w8a8_quant_act_rowwise_hadamard   the same on Hadamard-rotated rows
+  w8a8_hadamard_rotate          rows rotated by the block Walsh-Hadamard matrix -> bf16
   w8a8_linear                   8-bit product + fused dequant epilogue -> bf16
   w8a8_linear_backward_dx       dX = dY . W from quantized dY and W^T codes
   w8a8_gemm_i32                 raw int32 accumulators (test export)
@@ -64,6 +66,8 @@ def _load_library():
         "svdq_prepare_subspace": (I64, [I64]),
         "svdq_prepare_workspace_bytes": (ctypes.c_size_t, [I64, I64, I64]),
         "svdq_prepare": (I, [P, I64, I64, I64, P, I, P, P, P, P, P, P]),
+        "w8a8_quant_act_rowwise_hadamard": (I, [I, P, I64, I64, I64, P, I64, P, P]),
+        "w8a8_hadamard_rotate": (I, [P, I64, I64, I64, P, I64, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -161,6 +165,29 @@ def w8a8_quant_act_rowwise(x, qtype=INT8, ldq=None, out=None, scale=None):
     s = scale if scale is not None else torch.empty(M, dtype=torch.float32, device=dev)
     _check(_lib.w8a8_quant_act_rowwise(qtype, _ptr(x), M, K, ldx, _ptr(xq), ldq, _ptr(s), _stream(dev)))
     return xq, s
+
+
+def w8a8_quant_act_rowwise_hadamard(x, qtype=INT8, ldq=None, out=None, scale=None):
+    """x: bf16 [M, K], K % 16 == 0.  Codes [M, ldq] and scales [M] of the Hadamard-rotated rows."""
+    _need(x, torch.bfloat16, "x")
+    x = x.contiguous()
+    M, K = x.shape
+    ldq = ldq if ldq is not None else K
+    dev = x.device
+    xq = out if out is not None else torch.empty((M, ldq), dtype=_code_dtype(qtype), device=dev)
+    s = scale if scale is not None else torch.empty(M, dtype=torch.float32, device=dev)
+    _check(_lib.w8a8_quant_act_rowwise_hadamard(qtype, _ptr(x), M, K, K, _ptr(xq), ldq, _ptr(s), _stream(dev)))
+    return xq, s
+
+
+def w8a8_hadamard_rotate(x, out=None):
+    """x: bf16 [M, K], K % 16 == 0 -> bf16 [M, K] rotated rows."""
+    _need(x, torch.bfloat16, "x")
+    x = x.contiguous()
+    M, K = x.shape
+    y = out if out is not None else torch.empty((M, K), dtype=torch.bfloat16, device=x.device)
+    _check(_lib.w8a8_hadamard_rotate(_ptr(x), M, K, K, _ptr(y), K, _stream(x.device)))
+    return y
 
 
 # --------------------------------------------------------------- the linear

@@ -185,10 +185,13 @@ __global__ __launch_bounds__(256) void act_quant_rowwise_2pass_kernel(const uint
 template <int QT>
 void launch_act_quant(const uint16_t *x, int64_t M, int K, int64_t ldx, uint8_t *xq, int64_t ldq, float *scale,
                       hipStream_t stream) {
-    // Single-pass kernel: about two workgroups per CU, each wave walking
+    // Single-pass kernel: up to four workgroups per CU, each wave walking
     // rows with a stride of the whole grid (two rows in flight per wave).
     const int64_t blocks = (M + kRowsPerBlock - 1) / kRowsPerBlock;
-    const int64_t cap = 2 * (int64_t)device_cu_count();
+#ifndef W8A8_ACTQ_WG_PER_CU
+#define W8A8_ACTQ_WG_PER_CU 4  // workgroups (4 rows each) per CU: one row per wave at M = 16 x CUs
+#endif
+    const int64_t cap = W8A8_ACTQ_WG_PER_CU * (int64_t)device_cu_count();
     const dim3 grid((unsigned)(blocks < cap ? blocks : cap)), block(64 * kRowsPerBlock);
     const dim3 grid2((unsigned)blocks);
     const int cpl = (((K + 7) / 8) + 63) / 64;  // 16-byte chunks per lane
