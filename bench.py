@@ -37,11 +37,14 @@ AQ_ITERS = 200
 def _args():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    # Under this load the GPU settles at a power-limited clock after ~30 ms of
+    # work; shorter warm-ups time the ramp (launch times swing by +-20% there).
+    p.add_argument("--steps", type=int, default=400)
+    p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-rows", action="store_true", help="skip the per-row figures of the other paths")
-    p.add_argument("--cpu-rows", type=int, default=96, help="rows of the oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=1024,
+                   help="rows of the oracle sample (about 15 s of one CPU core)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 512 MiB device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -52,14 +55,20 @@ def _bf16(t_bits):
     return torch.from_numpy(np.ascontiguousarray(t_bits).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def _time_launches(fn, iters, warmup):
+def _time_launches(fn, iters, warmup, prefill=False):
     """Average duration (ms) of fn(i) over iters launches, HIP events on the
-    current stream (the stream the library launches on)."""
+    current stream (the stream the library launches on).
+
+    prefill: for kernels about as short as the Python call that launches them
+    (~8 us), the launches are queued behind a short GPU spin first, so that the
+    GPU runs them back to back instead of waiting for the host."""
     import torch
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if prefill:
+        torch.cuda._sleep(1_000_000 + 50_000 * iters)   # ~25 us of spin per queued launch
     e0.record()
     for i in range(iters):
         fn(i)
@@ -175,7 +184,7 @@ def main():
     # ---- per-kernel averages (same launches, timed apart); the act-quant
     # kernel on its own input sets, enough of them that each launch reads cold HBM
     iters = max(args.steps, 20)
-    ms_gemm = _time_launches(gemm, iters, 5)
+    ms_gemm = _time_launches(gemm, iters, 100)
     aq_sets = [(sets[0]["x"].clone(), torch.empty((M, K), dtype=torch.int8, device="cuda"),
                 torch.empty(M, dtype=torch.float32, device="cuda")) for _ in range(AQ_ROTATE)]
 
@@ -183,7 +192,7 @@ def main():
         xa, qa, sa = aq_sets[i % AQ_ROTATE]
         w8.w8a8_quant_act_rowwise(xa, out=qa, scale=sa)
 
-    ms_aq = _time_launches(act_quant_cold, AQ_ITERS, 2 * AQ_ROTATE)
+    ms_aq = _time_launches(act_quant_cold, AQ_ITERS, 2 * AQ_ROTATE, prefill=True)
     del aq_sets
     gemm_tops = ops / (ms_gemm * 1e-3) / 1e12
     aq_bytes = 2.0 * M * K + M * K + 4.0 * M
@@ -232,10 +241,19 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def _time_row(fn, settle_ms=30.0, span_ms=30.0):
+    """_time_launches sized by time: ~settle_ms of untimed launches (the clock
+    settles under load), then launches covering ~span_ms; short kernels are
+    queued behind a spin (prefill)."""
+    est = _time_launches(fn, 2, 1)
+    warm = max(3, int(settle_ms / est))
+    iters = min(2000, max(10, int(span_ms / est)))
+    return _time_launches(fn, iters, warm, prefill=est < 0.04)
+
+
 def other_rows(w8, torch, workloads, args):
     """Per-kernel figures of the other hot-path rows (not part of `value`)."""
     res = {}
-    iters = 20
     # SVDQuant at the headline shape, r = 32
     d = workloads.svdq()
     x, l1, l2, rr, b = (_bf16(d[k]) for k in ("x", "l1", "l2", "r", "bias"))
@@ -244,8 +262,8 @@ def other_rows(w8, torch, workloads, args):
     xq = torch.empty((M, K), dtype=torch.int8, device="cuda")
     sx = torch.empty(M, dtype=torch.float32, device="cuda")
     ws = torch.empty(w8.svdq_workspace_bytes(M, 32), dtype=torch.uint8, device="cuda")
-    ms = _time_launches(lambda i: w8.svdq_linear(x, rq, sr, l1, l2, b, out=y, xq_out=xq, x_scale_out=sx,
-                                                 workspace=ws), iters, 3)
+    ms = _time_row(lambda i: w8.svdq_linear(x, rq, sr, l1, l2, b, out=y, xq_out=xq, x_scale_out=sx,
+                                                 workspace=ws))
     ops = 2.0 * M * N * K + 2.0 * M * K * 32 + 2.0 * M * 32 * N
     res["svdq_linear_M4096_K3072_N12288_r32"] = {"us": round(ms * 1e3, 1), "TOPS": round(ops / ms / 1e9, 1)}
     del x, l1, l2, rr, b, rq, y, xq, ws
@@ -258,7 +276,7 @@ def other_rows(w8, torch, workloads, args):
         bb = _bf16(d[bk])
         nn = wq.shape[0]
         y = torch.empty((4608, nn), dtype=torch.bfloat16, device="cuda")
-        ms = _time_launches(lambda i: w8.w8a8_linear(xq, sx, wq, sw, bb, out=y), iters, 3)
+        ms = _time_row(lambda i: w8.w8a8_linear(xq, sx, wq, sw, bb, out=y))
         res[name] = {"us": round(ms * 1e3, 1), "TOPS": round(2.0 * 4608 * nn * 3072 / ms / 1e9, 1)}
     del x, xq, y
     # fp8 train step shapes
@@ -267,62 +285,66 @@ def other_rows(w8, torch, workloads, args):
     x = _bf16(d["x"])
     xq, sx = w8.w8a8_quant_act_rowwise(x, qtype=w8.FP8_E4M3)
     y = torch.empty((8192, N), dtype=torch.bfloat16, device="cuda")
-    ms = _time_launches(lambda i: w8.w8a8_linear(xq, sx, wq, sw, out=y), iters, 3)
+    ms = _time_row(lambda i: w8.w8a8_linear(xq, sx, wq, sw, out=y))
     res["fp8_fwd_M8192_K3072_N12288"] = {"us": round(ms * 1e3, 1),
                                          "TFLOPS": round(2.0 * 8192 * N * K / ms / 1e9, 1)}
     dy = _bf16(d["dy"])
     dyq = torch.empty((8192, N), dtype=torch.float8_e4m3fn, device="cuda")
     sdy = torch.empty(8192, dtype=torch.float32, device="cuda")
-    ms = _time_launches(lambda i: w8.w8a8_quant_act_rowwise(dy, qtype=w8.FP8_E4M3, out=dyq, scale=sdy), iters, 3)
+    ms = _time_row(lambda i: w8.w8a8_quant_act_rowwise(dy, qtype=w8.FP8_E4M3, out=dyq, scale=sdy))
     bytes_ = 3.0 * 8192 * N + 4 * 8192
     res["act_quant_fp8_dY_8192x12288"] = {"us": round(ms * 1e3, 1), "GB/s": round(bytes_ / ms / 1e6, 1)}
     dx = torch.empty((8192, K), dtype=torch.bfloat16, device="cuda")
-    ms = _time_launches(lambda i: w8.w8a8_linear_backward_dx(dyq, sdy, wqt, sw, out=dx), iters, 3)
+    ms = _time_row(lambda i: w8.w8a8_linear_backward_dx(dyq, sdy, wqt, sw, out=dx))
     res["fp8_bwd_dx_M8192_N12288_K3072"] = {"us": round(ms * 1e3, 1),
                                             "TFLOPS": round(2.0 * 8192 * N * K / ms / 1e9, 1)}
     # the int8 analogue of the train step's dX
     wq8, wqt8, sw8 = w8.w8a8_quant_weight_tensorwise(_bf16(d["w"]), qtype=w8.INT8, transposed=True)
     dyq8, sdy8 = w8.w8a8_quant_act_rowwise(dy, qtype=w8.INT8)
-    ms = _time_launches(lambda i: w8.w8a8_linear_backward_dx(dyq8, sdy8, wqt8, sw8, out=dx), iters, 3)
+    ms = _time_row(lambda i: w8.w8a8_linear_backward_dx(dyq8, sdy8, wqt8, sw8, out=dx))
     res["int8_bwd_dx_M8192_N12288_K3072"] = {"us": round(ms * 1e3, 1),
                                              "TOPS": round(2.0 * 8192 * N * K / ms / 1e9, 1)}
     del wq, wqt, x, xq, y, dy, dyq, dx, wq8, wqt8, dyq8
-    # Q8_0
-    v = torch.from_numpy(workloads.q8_0_vector()).cuda()
-    n = v.numel()
-    blob = torch.empty(w8.q8_0_nbytes(n), dtype=torch.uint8, device="cuda")
-    out = torch.empty(n, dtype=torch.float32, device="cuda")
-    ms = _time_launches(lambda i: w8.q8_0_quantize(v, out=blob), iters, 3)
+    # Q8_0 (4 buffer sets of 85 MB: every launch reads cold HBM, not the 256 MB Infinity Cache)
+    v0 = torch.from_numpy(workloads.q8_0_vector()).cuda()
+    n = v0.numel()
+    qs = [(v0 if j == 0 else v0.clone(), torch.empty(w8.q8_0_nbytes(n), dtype=torch.uint8, device="cuda"),
+           torch.empty(n, dtype=torch.float32, device="cuda")) for j in range(4)]
+    ms = _time_row(lambda i: w8.q8_0_quantize(qs[i % 4][0], out=qs[i % 4][1]))
     qbytes = 4.0 * n + w8.q8_0_nbytes(n)
     res["q8_0_quantize_n16777221"] = {"us": round(ms * 1e3, 1), "GB/s": round(qbytes / ms / 1e6, 1)}
-    ms = _time_launches(lambda i: w8.q8_0_dequantize(blob, n, out=out), iters, 3)
+    ms = _time_row(lambda i: w8.q8_0_dequantize(qs[i % 4][1], n, out=qs[i % 4][2]))
     res["q8_0_dequantize_n16777221"] = {"us": round(ms * 1e3, 1), "GB/s": round(qbytes / ms / 1e6, 1)}
-    del v, blob, out
+    del v0, qs
     # GGUF A8: Q8_0 weight [12288, 3072] -> per-channel int8 / e4m3, then the linear at the headline shape
     d = workloads.gguf()
     gb = torch.from_numpy(d["w_blocks"]).cuda()
     x = _bf16(d["x"])
     bb = _bf16(d["bias"])
     y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    gbs = [gb] + [gb.clone() for _ in range(3)]    # 4 x 78 MB moved per launch: cold HBM
     for qt, tag in ((w8.INT8, "int8"), (w8.FP8_E4M3, "fp8")):
-        wq = torch.empty((N, K), dtype=torch.int8 if qt == w8.INT8 else torch.float8_e4m3fn, device="cuda")
-        sw = torch.empty(N, dtype=torch.float32, device="cuda")
-        ms = _time_launches(lambda i: w8.gguf_a8_requant_q8_0(gb, N, K, qtype=qt, out=wq, scale=sw), iters, 3)
+        wqs = [torch.empty((N, K), dtype=torch.int8 if qt == w8.INT8 else torch.float8_e4m3fn, device="cuda")
+               for _ in range(4)]
+        sws = [torch.empty(N, dtype=torch.float32, device="cuda") for _ in range(4)]
+        ms = _time_row(lambda i: w8.gguf_a8_requant_q8_0(gbs[i % 4], N, K, qtype=qt, out=wqs[i % 4], scale=sws[i % 4]))
+        wq, sw = wqs[0], sws[0]
         rbytes = 1.0 * gb.numel() + N * K + 4.0 * N  # blocks read once, codes and scales written
         res[f"gguf_a8_requant_{tag}_N12288_K3072"] = {"us": round(ms * 1e3, 1), "GB/s": round(rbytes / ms / 1e6, 1)}
         xq, sx = w8.w8a8_quant_act_rowwise(x, qtype=qt)
-        ms = _time_launches(lambda i: w8.gguf_a8_linear(xq, sx, wq, sw, bb, out=y), iters, 3)
+        ms = _time_row(lambda i: w8.gguf_a8_linear(xq, sx, wq, sw, bb, out=y))
         res[f"gguf_a8_linear_{tag}_M4096_K3072_N12288"] = {"us": round(ms * 1e3, 1),
                                                            "TOPS": round(2.0 * M * N * K / ms / 1e9, 1)}
     # act-quant of the headline X with the Hadamard rotation fused (K = 3072: three 1024-blocks)
     d = workloads.svdq()
-    xh = _bf16(d["x"])
-    xqh = torch.empty((M, K), dtype=torch.int8, device="cuda")
-    sxh = torch.empty(M, dtype=torch.float32, device="cuda")
-    ms = _time_launches(lambda i: w8.w8a8_quant_act_rowwise_hadamard(xh, out=xqh, scale=sxh), iters, 3)
+    xh0 = _bf16(d["x"])
+    hs = [(xh0.clone(), torch.empty((M, K), dtype=torch.int8, device="cuda"),
+           torch.empty(M, dtype=torch.float32, device="cuda")) for _ in range(AQ_ROTATE)]
+    ms = _time_row(lambda i: w8.w8a8_quant_act_rowwise_hadamard(hs[i % AQ_ROTATE][0], out=hs[i % AQ_ROTATE][1],
+                                                                scale=hs[i % AQ_ROTATE][2]))
     res["act_quant_hadamard_int8_X4096x3072"] = {"us": round(ms * 1e3, 1),
                                                  "GB/s": round((3.0 * M * K + 4 * M) / ms / 1e6, 1)}
-    del xh, xqh
+    del xh0, hs
     # SVDQuant weight preparation of the SVDQuant workload's weight, r = 32, 2 power iterations
     d = workloads.svdq()
     l2p, l1p, rp = (torch.from_numpy(workloads.bf16_bits_to_f32(d[k])).double() for k in ("l2", "l1", "r"))
