@@ -127,7 +127,10 @@ __device__ __forceinline__ v16f low_rank_add(const GemmArgs &p, v16f v, int nbas
 }
 
 
-template <int QT, int EPI>
+// TAIL: K is not a multiple of BK * NST, so some stages reach past K and
+// need per-lane range checks; otherwise every stage is whole and the stage's
+// K offset travels in the instruction's scalar offset.
+template <int QT, int EPI, bool TAIL>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     // One distinct array per stage, so the compiler can tell the LDS-DMA writes
     // into one stage from the fragment reads of another and does not wait for
@@ -204,15 +207,22 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         constexpr int P = decltype(part_c)::value, NP = decltype(np_c)::value;
         constexpr int lo = P * kLoadsPerStage / NP, hi = (P + 1) * kLoadsPerStage / NP;
         const int k0 = ld_kt * BK;
-        const bool full = k0 + BK <= K;
+        const bool full = !TAIL || k0 + BK <= K;
         [&]<int... J>(std::integer_sequence<int, J...>) {
             (([&] {
                  constexpr int j = lo + J;
                  constexpr int i = j % kLoadsPerOp;
                  constexpr int grp = i / kImmLoads, imm = (i % kImmLoads) * 1024;
-                 const int o = full ? goff[i] + k0 : (k0 + gcol[i] < K ? goff[i] + k0 : kOobOffset);
                  uint8_t *m0 = stage + (j < kLoadsPerOp ? 0 : kOpBytes) + wave * 64 * BK + grp * kImmLoads * 1024;
-                 __builtin_amdgcn_raw_ptr_buffer_load_lds(j < kLoadsPerOp ? rx : rw, (lds_ptr_t)m0, 16, o, 0, imm, 0);
+                 if constexpr (TAIL) {
+                     const int o = full ? goff[i] + k0 : (k0 + gcol[i] < K ? goff[i] + k0 : kOobOffset);
+                     __builtin_amdgcn_raw_ptr_buffer_load_lds(j < kLoadsPerOp ? rx : rw, (lds_ptr_t)m0, 16, o, 0, imm,
+                                                              0);
+                 } else {
+                     // per-lane offset fixed for the whole kernel, stage offset scalar
+                     __builtin_amdgcn_raw_ptr_buffer_load_lds(j < kLoadsPerOp ? rx : rw, (lds_ptr_t)m0, 16, goff[i], k0,
+                                                              imm, 0);
+                 }
              }()),
              ...);
         }(std::make_integer_sequence<int, hi - lo>{});
@@ -548,7 +558,8 @@ void launch(const GemmArgs &a, hipStream_t stream) {
     const int tm = (a.M + BM - 1) / BM, tn = (a.N + BN - 1) / BN;
     const int tiles = tm * tn;
     const int grid = tiles < device_cu_count() ? tiles : device_cu_count();
-    gemm_kernel<QT, EPI><<<grid, kThreads, 0, stream>>>(a, tm, tn);
+    if (a.K % (BK * NST) == 0) gemm_kernel<QT, EPI, false><<<grid, kThreads, 0, stream>>>(a, tm, tn);
+    else gemm_kernel<QT, EPI, true><<<grid, kThreads, 0, stream>>>(a, tm, tn);
 }
 
 }  // namespace
