@@ -377,6 +377,31 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         advance_cursor();
     };
     static_assert(NST % 2 == 0 || KSTEPS % 2 == 0, "fragment parity must restart at each stage group");
+    // stages FROM .. TO-1 of a group of NST
+    auto run_stages = [&](auto from_c, auto to_c, auto first_c) {
+        constexpr int F = decltype(from_c)::value, T = decltype(to_c)::value;
+        [&]<int... S>(std::integer_sequence<int, S...>) {
+            (run_stage(std::integral_constant<int, F + S>{}, first_c), ...);
+        }(std::make_integer_sequence<int, T - F>{});
+    };
+
+    // Interior tiles: the row scales (128 f32) and bias (128 bf16) of this
+    // wave's outputs go to the start of its staging area by LDS-DMA while the
+    // tile's last stages are multiplied, so the epilogue does not open with a
+    // global load queued behind the next tile's prefetches.  Lanes past the
+    // 512 (256) bytes read out of range and write zeros after them.
+    constexpr int kEpiSx = 0, kEpiBias = 1024;
+    auto epi_dma = [&](int mw, int nw) {
+        uint8_t *ob = obuf + wave * kOutWaveBytes;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(p.sx + mw), (short)0, 512, kBufferRsrcWord3);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(ob + kEpiSx), 16, lane * 16, 0, 0, 0);
+        if (p.bias) {
+            const __amdgpu_buffer_rsrc_t rb =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(p.bias + nw), (short)0, 256, kBufferRsrcWord3);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(ob + kEpiBias), 16, lane * 16, 0, 0, 0);
+        }
+    };
 
     // Prologue: stages 0 .. NST-2 in flight, wait for stage 0.
     [&]<int... S>(std::integer_sequence<int, S...>) {
@@ -410,7 +435,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
             const int m = mw + mb * 32 + erow;
-            tm[mb] = (kIn || m < M) ? p.sx[m] * sw : 0.0f;
+            if constexpr (kIn) tm[mb] = *reinterpret_cast<const float *>(ob + kEpiSx + (mb * 32 + erow) * 4) * sw;
+            else tm[mb] = m < M ? p.sx[m] * sw : 0.0f;
         }
         if constexpr (kCol) {
 #pragma unroll
@@ -433,7 +459,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                 const int n = nw + nb * 32 + 8 * j + 4 * ehalf;
                 uint2 b = make_uint2(0u, 0u);
                 if (p.bias) {
-                    if (kIn || ((N & 3) == 0 && n < N)) {
+                    if constexpr (kIn) {
+                        b = *reinterpret_cast<const uint2 *>(ob + kEpiBias + (n - nw) * 2);
+                    } else if ((N & 3) == 0 && n < N) {
                         b = *reinterpret_cast<const uint2 *>(p.bias + n);
                     } else {
                         uint32_t w[4];
@@ -501,14 +529,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         // the previous tile's last stage read are dead across its epilogue.
         read_frags(lds0, 0, fa[0], fb[0]);
 
-        // the first NST stages start the accumulators (kt_end >= NST)
-        [&]<int... S>(std::integer_sequence<int, S...>) {
-            (run_stage(std::integral_constant<int, S>{}, std::true_type{}), ...);
-        }(std::make_integer_sequence<int, NST>{});
+        // Interior tiles (all rows and columns in range, N % 8 == 0) take a
+        // copy of the epilogue without any bounds checks.
+        const bool interior = tc.m0 + BM <= M && tc.n0 + BN <= N && (N & 7) == 0;
+        constexpr bool kDma = EPI != kEpiI32;
+        // The first NST stages start the accumulators (kt_end >= NST).  The
+        // epilogue inputs are fetched before the second-to-last stage: the
+        // waits at the ends of the last two stages cover them.
+        run_stages(std::integral_constant<int, 0>{}, std::integral_constant<int, NST>{}, std::true_type{});
         for (int kt0 = NST; kt0 < kt_end; kt0 += NST) {
-            [&]<int... S>(std::integer_sequence<int, S...>) {
-                (run_stage(std::integral_constant<int, S>{}, std::false_type{}), ...);
-            }(std::make_integer_sequence<int, NST>{});
+            run_stages(std::integral_constant<int, 0>{}, std::integral_constant<int, NST - 2>{}, std::false_type{});
+            if constexpr (kDma) {
+                if (interior && kt0 + NST == kt_end) epi_dma(mw, nw);
+            }
+            run_stages(std::integral_constant<int, NST - 2>{}, std::integral_constant<int, NST>{}, std::false_type{});
+        }
+        if constexpr (kDma) {
+            if (interior && kt_end == NST) {
+                epi_dma(mw, nw);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
         }
 
         // --------------------------------------------------------- epilogue
@@ -538,9 +578,6 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                     }
                 }
         } else {
-            // Interior tiles (all 256 rows and columns in range, N % 8 == 0)
-            // take a copy of the epilogue without any bounds checks.
-            const bool interior = tc.m0 + BM <= M && tc.n0 + BN <= N && (N & 7) == 0;
             if (interior) bf16_epilogue(std::true_type{}, mw, nw);
             else bf16_epilogue(std::false_type{}, mw, nw);
         }
