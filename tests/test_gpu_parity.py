@@ -365,7 +365,9 @@ def test_q8_0_full_config():
 
 # ------------------------------------------------------------ GGUF A8
 @pytest.mark.parametrize("qt", [INT8, FP8])
-@pytest.mark.parametrize("N,K", [(1, 32), (5, 64), (37, 160), (130, 2048), (9, 2080), (7, 4128), (300, 3072)])
+# K = 15392: the longest row staged whole (481 blocks); K = 16384: rows streamed in chunks
+@pytest.mark.parametrize("N,K", [(1, 32), (5, 64), (37, 160), (130, 2048), (9, 2080), (7, 4128), (300, 3072),
+                                 (3, 15392), (5, 16384)])
 def test_gguf_a8_requant(qt, N, K):
     _say(f"gguf a8 requant qt={qt} N={N} K={K}")
     rng = np.random.default_rng(N * 7 + K)

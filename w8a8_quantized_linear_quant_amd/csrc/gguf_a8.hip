@@ -9,11 +9,14 @@
 // of an f16 scale d and 32 int8 codes); a weight row of K values is K / 32
 // consecutive blocks, and its values are the exact dequantization q * d.
 //
-// One wave per output row.  The row is streamed through the wave's LDS area
-// in chunks of 64 blocks (2176 bytes, fetched with 16-byte loads from the
-// 16-byte aligned address at or below the chunk), then 8 lanes take one block
-// (4 codes each).  Pass 1 finds the row absmax, pass 2 re-stages the row (an
-// L2 hit) and writes the codes: 8 blocks = 256 contiguous bytes per step.
+// One wave per output row.  Rows of up to kMaxRowBytes are staged whole in
+// the wave's LDS area (16-byte loads from the 16-byte aligned address at or
+// below the row); 8 lanes take one block (4 codes each) to find the row
+// absmax, then quantize the staged values, writing the codes in place over
+// the blocks they come from (block b's 32 codes land at 32 b, at or before
+// its source bytes), and the row leaves as 16-byte stores.  Longer rows are
+// streamed through the LDS area in chunks of 64 blocks in two passes (absmax,
+// then codes, the second re-staging the row from L2).
 #include "internal.hpp"
 
 namespace w8a8 {
@@ -23,6 +26,103 @@ constexpr int kThreads = 256;            // 4 waves, one row each
 constexpr int kChunkBlocks = 64;
 constexpr int kStageBytes = kChunkBlocks * 34 + 32;  // chunk + alignment slack, multiple of 16
 static_assert(kStageBytes % 16 == 0, "16-byte staging");
+constexpr int kMaxRowBytes = 16 * 1024 - 16;  // single-pass limit: 4 waves x 16 KB of LDS
+
+// Whole-row kernel: each wave stages one row of row_stage bytes (a multiple
+// of 16, at least the row's bytes + 15) in dynamic LDS.
+template <int QT>
+__global__ __launch_bounds__(kThreads) void gguf_a8_requant_row_kernel(const uint8_t *__restrict__ blocks,
+                                                                       uint32_t total_bytes, int N, int K,
+                                                                       int row_stage, uint8_t *__restrict__ wq,
+                                                                       float *__restrict__ scale) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t dyn_lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    uint8_t *st = dyn_lds + wave * row_stage;
+    const int nb = K / 32;
+    const uint32_t row_bytes = (uint32_t)nb * 34u;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(blocks), (short)0, (int)total_bytes, kBufferRsrcWord3);
+    const float qmax = QT == W8A8_INT8 ? 127.0f : 448.0f;
+    const int blk_in_step = lane >> 3, part = lane & 7;  // 8 lanes per block, 4 codes each
+
+    for (int n = blockIdx.x * (kThreads / 64) + wave; n < N; n += gridDim.x * (kThreads / 64)) {
+        const uint32_t s0 = (uint32_t)n * row_bytes;
+        const uint32_t a0 = s0 & ~15u;
+        const int off = (int)(s0 - a0);
+        const int nvec = (off + (int)row_bytes + 15) / 16;
+        for (int i = lane; i < nvec; i += 64) {
+            const uint32_t vo = a0 + 16u * i;
+            v4u v;
+            if (vo + 16u <= total_bytes) {
+                v = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0));
+            } else {
+                // the tensor's last 16 bytes run past its end: a wide load
+                // that crosses num_records reads zero as a whole, so take the
+                // remaining bytes one by one
+                uint8_t t[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) t[j] = __builtin_amdgcn_raw_buffer_load_b8(rs, vo + j, 0, 0);
+                v = __builtin_bit_cast(v4u, t);
+            }
+            *reinterpret_cast<v4u *>(st + 16 * i) = v;
+        }
+        // values of this lane's 4 codes of block b (b < nb)
+        auto block_vals = [&](int b, float *v) {
+            const uint8_t *bp = st + off + b * 34;
+            const uint32_t dbits = *reinterpret_cast<const uint16_t *>(bp);
+            const uint32_t lo = *reinterpret_cast<const uint16_t *>(bp + 2 + 4 * part);
+            const uint32_t hi = *reinterpret_cast<const uint16_t *>(bp + 4 + 4 * part);
+            const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)dbits);
+            const uint32_t w = lo | (hi << 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = (float)(int8_t)(w >> (8 * i)) * d;  // exact in f32
+        };
+        // row absmax (non-negative floats order like their bit patterns)
+        uint32_t amax_bits = 0;
+        for (int b0 = 0; b0 < nb; b0 += 8) {
+            const int b = b0 + blk_in_step;
+            if (b < nb) {
+                float v[4];
+                block_vals(b, v);
+                const float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+                amax_bits = max(amax_bits, __float_as_uint(a));
+            }
+        }
+        const float s = absmax_scale(__uint_as_float(wave_max_u32(amax_bits)), qmax);
+        const float r = 1.0f / s;
+        if (lane == 0) scale[n] = s;
+        // codes, in place: the reads of a step (blocks b0..b0+7 at >= 34 b0)
+        // precede its writes (32 b0 .. 32 b0 + 255) in the wave's LDS order,
+        // and later steps read from 34 (b0 + 8) > 32 b0 + 255 on
+        for (int b0 = 0; b0 < nb; b0 += 8) {
+            const int b = b0 + blk_in_step;
+            if (b < nb) {
+                float v[4];
+                block_vals(b, v);
+                uint32_t word = 0;
+                if constexpr (QT == W8A8_INT8) {
+                    // |v / s| <= 127 by the scale rule: no clamp needed; the
+                    // add of 1.5 * 2^23 rounds half to even
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        word |= (__float_as_uint(quotient_nosign(v[i], s, r) + 12582912.0f) & 0xFFu) << (8 * i);
+                } else {
+                    float q[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) q[i] = __builtin_amdgcn_fmed3f(quotient(v[i], s, r), -448.0f, 448.0f);
+                    int pk = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+                    pk = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], pk, true);
+                    word = (uint32_t)pk;
+                }
+                *reinterpret_cast<uint32_t *>(st + b * 32 + 4 * part) = word;
+            }
+        }
+        uint8_t *orow = wq + (size_t)n * K;
+        for (int i = lane; i < K / 16; i += 64)
+            *reinterpret_cast<v4u *>(orow + 16 * i) = *reinterpret_cast<const v4u *>(st + 16 * i);
+    }
+}
 
 template <int QT>
 __global__ __launch_bounds__(kThreads) void gguf_a8_requant_kernel(const uint8_t *__restrict__ blocks,
@@ -147,6 +247,20 @@ extern "C" w8a8_status gguf_a8_requant_q8_0(w8a8_qtype qtype, const void *blocks
     int64_t grid = (N + rows_per_wg - 1) / rows_per_wg;
     const int64_t cap = 8LL * device_cu_count();
     if (grid > cap) grid = cap;
+    const int64_t row_bytes = (K / 32) * 34;
+    if (row_bytes <= kMaxRowBytes) {
+        const int row_stage = (int)((row_bytes + 15 + 15) / 16 * 16);
+        const size_t lds = (size_t)row_stage * rows_per_wg;
+        if (qtype == W8A8_INT8)
+            gguf_a8_requant_row_kernel<W8A8_INT8><<<(int)grid, kThreads, lds, stream>>>(
+                static_cast<const uint8_t *>(blocks), (uint32_t)total, (int)N, (int)K, row_stage,
+                static_cast<uint8_t *>(wq), w_scale);
+        else
+            gguf_a8_requant_row_kernel<W8A8_FP8_E4M3><<<(int)grid, kThreads, lds, stream>>>(
+                static_cast<const uint8_t *>(blocks), (uint32_t)total, (int)N, (int)K, row_stage,
+                static_cast<uint8_t *>(wq), w_scale);
+        return launch_status();
+    }
     if (qtype == W8A8_INT8)
         gguf_a8_requant_kernel<W8A8_INT8><<<(int)grid, kThreads, 0, stream>>>(
             static_cast<const uint8_t *>(blocks), (uint32_t)total, (int)N, (int)K, static_cast<uint8_t *>(wq), w_scale);
