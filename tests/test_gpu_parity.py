@@ -352,6 +352,22 @@ def test_q8_0_small(n):
     assert_equal(y.cpu().numpy().view(np.uint32), oracle.q8_0_dequantize(ref, n).view(np.uint32), "dequant")
 
 
+def test_q8_0_exact_ties():
+    """Blocks whose quotients value / scale fall exactly half-way between
+    integers, with scales 1, 3 and 2^-3 (3 has an inexact reciprocal): the
+    kernel's quotient must round like the IEEE division before the RNE."""
+    rng = np.random.default_rng(5)
+    halves = (rng.integers(-127, 127, (30, 32)) + 0.5).astype(np.float64)
+    halves[:, 0] = 127.0                        # the block absmax: scale = c exactly
+    halves[:, 1] = -126.5
+    blocks = [halves[i] * c for i, c in enumerate([1.0, 3.0, 0.125] * 10)]
+    v = np.concatenate(blocks).astype(np.float32)
+    assert np.array_equal(v.astype(np.float64), np.concatenate(blocks))   # exact in f32
+    blob = W8.q8_0_quantize(f32_dev(v))
+    torch.cuda.synchronize()
+    assert_equal(bytes_host(blob), oracle.q8_0_quantize(v), "q8_0 bytes on ties")
+
+
 def test_q8_0_full_config():
     _say("q8_0 n=16,777,221 full")
     v = workloads.q8_0_vector()
@@ -372,6 +388,32 @@ def test_gguf_a8_requant(qt, N, K):
     _say(f"gguf a8 requant qt={qt} N={N} K={K}")
     rng = np.random.default_rng(N * 7 + K)
     blob = workloads.q8_0_weight_blocks(rng, N, K, zero_rows=1)
+    wq, s = W8.gguf_a8_requant_q8_0(torch.from_numpy(blob).cuda(), N, K, qtype=qt)
+    torch.cuda.synchronize()
+    ref_q, ref_s = oracle.gguf_a8_requant_q8_0(qt, blob, N, K)
+    assert_equal(s.cpu().numpy().view(np.uint32), ref_s.view(np.uint32), "scales")
+    assert_equal(bytes_host(wq), ref_q, "codes")
+
+
+@pytest.mark.parametrize("qt", [INT8, FP8])
+def test_gguf_a8_requant_exact_ties(qt):
+    """Rows whose absmax is 127 d1 with d1 in {1, 3, 0.75} and whose other
+    blocks have d = d1 / 2 and odd codes: every such value / scale is an odd
+    multiple of 1/2, a tie of the int8 rounding."""
+    rng = np.random.default_rng(6)
+    N, K = 6, 256
+    nb = K // 32
+    d = np.empty((N, nb), np.float16)
+    q = rng.integers(-63, 64, (N, nb, 32)) * 2 + 1          # odd codes
+    for n, d1 in enumerate([1.0, 3.0, 0.75] * 2):
+        d[n] = np.float16(d1 / 2)
+        d[n, 0] = np.float16(d1)
+        q[n, 0] = rng.integers(-127, 128, 32)
+        q[n, 0, 3] = 127
+    blob = np.empty((N * nb, 34), np.uint8)
+    blob[:, :2] = d.reshape(-1).view(np.uint8).reshape(-1, 2)
+    blob[:, 2:] = q.reshape(-1, 32).astype(np.int8).view(np.uint8)
+    blob = blob.ravel()
     wq, s = W8.gguf_a8_requant_q8_0(torch.from_numpy(blob).cuda(), N, K, qtype=qt)
     torch.cuda.synchronize()
     ref_q, ref_s = oracle.gguf_a8_requant_q8_0(qt, blob, N, K)

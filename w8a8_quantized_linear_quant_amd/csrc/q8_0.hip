@@ -54,12 +54,15 @@ __global__ __launch_bounds__(kThreads) void q8_0_quantize_kernel(const float *__
             float a = fmaxf(fmaxf(fabsf(v[u][0]), fabsf(v[u][1])), fmaxf(fabsf(v[u][2]), fabsf(v[u][3])));
             a = group8_max(a);
             const float s = absmax_scale(a, 127.0f);
+            const float r = 1.0f / s;
             uint32_t word = 0;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                // the page divides value / scale: IEEE division, then RNE
-                const float q = __builtin_amdgcn_fmed3f(v[u][i] / s, -128.0f, 127.0f);
-                word |= ((uint32_t)(int)__builtin_rintf(q) & 0xFFu) << (8 * i);
+                // value / scale (the one-correction quotient equals the IEEE
+                // quotient down to 2^-20, below which both round to code 0),
+                // rounded half to even by the add of 1.5 * 2^23; |q| <= 127
+                // by the scale rule, so the page's clamp never acts
+                word |= (__float_as_uint(quotient_nosign(v[u][i], s, r) + 12582912.0f) & 0xFFu) << (8 * i);
             }
             uint8_t *blk = &stage[wave][u][(lane >> 3) * kBlockBytes];
             const int j = lane & 7;
