@@ -361,6 +361,14 @@ def other_rows(w8, torch, workloads, args):
                                                   workspace=ws), 5, 1)
     res["svdq_prepare_N12288_K3072_r32_iters2"] = {"us": round(ms * 1e3, 1)}
     torch.cuda.synchronize()
+    # each row against its own roofline: dense 8-bit MFMA (int8 5.0 POPS, fp8
+    # 5.0 PFLOP/s; the SVDQuant row's few bf16 flops are counted at that rate
+    # too) or HBM (8 TB/s)
+    for v in res.values():
+        for unit, bound, peak in (("TOPS", "mfma", PEAK_INT8_TOPS), ("TFLOPS", "mfma", PEAK_FP8_TFLOPS),
+                                  ("GB/s", "hbm", PEAK_HBM_GBS)):
+            if unit in v:
+                v.update(bound=bound, peak=peak, frac=round(v[unit] / peak, 4))
     return res
 
 
