@@ -98,8 +98,8 @@ __global__ __launch_bounds__(kThreads) void hadamard_act_quant_1024_kernel(const
 
     for (int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + wave; row < M; row += stride) {
         const uint16_t *xr = x + row * ldx;
-        float vb[NB][16];  // layout B values of every block
-        uint32_t amax_bits = 0;
+        float vb[NB][16];  // layout B values of every block, before the scale c
+        float amax = 0.0f;
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
             // layout A: lane l holds e = 16 l + t
@@ -141,20 +141,23 @@ __global__ __launch_bounds__(kThreads) void hadamard_act_quant_1024_kernel(const
                         u[t] = a + dd;
                         u[t + h] = a - dd;
                     }
-            // stages h = 256, 512 (lane bits 0, 1), then the scale c
+            // stages h = 256, 512 (lane bits 0, 1)
 #pragma unroll
             for (int t = 0; t < 16; ++t) u[t] = xlane_butterfly<0xB1>(u[t], sgn1);  // quad_perm [1,0,3,2]
 #pragma unroll
             for (int t = 0; t < 16; ++t) {
-                u[t] = xlane_butterfly<0x4E>(u[t], sgn2);  // quad_perm [2,3,0,1]
-                u[t] = u[t] * c;
-                vb[blk][t] = u[t];
-                amax_bits = max(amax_bits, __float_as_uint(u[t]) & 0x7FFFFFFFu);
+                vb[blk][t] = xlane_butterfly<0x4E>(u[t], sgn2);  // quad_perm [2,3,0,1]
+                amax = fmaxf(amax, fabsf(vb[blk][t]));
             }
         }
-        const float s = absmax_scale(__uint_as_float(wave_max_u32(amax_bits)), kQmax);
+        // The scale c = 2^-5 is exact, so it moves from the values to the
+        // divisor: scale from f32(amax c), codes from v / (32 s) with
+        // reciprocal f32(1 / s) / 32 -- the same numbers as (v c) / s and its
+        // one-correction quotient, scaled by a power of two.
+        const float s = absmax_scale(__uint_as_float(wave_max_u32(__float_as_uint(amax))) * c, kQmax);
         const float r = 1.0f / s;
         if (lane == 0) scale[row] = s;
+        const float s32 = s * 32.0f, r32 = r * c;
         uint8_t *qrow = xq + row * ldq;
         uint8_t *cb = reinterpret_cast<uint8_t *>(sb);  // 1 KB of codes per block
 #pragma unroll
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void hadamard_act_quant_1024_kernel(const
             // codes in layout B -> bytes at their element positions in LDS
 #pragma unroll
             for (int t4 = 0; t4 < 4; ++t4) {
-                const uint32_t w = codes4<QT>(&vb[blk][4 * t4], s, r);
+                const uint32_t w = codes4<QT>(&vb[blk][4 * t4], s32, r32);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) cb[lo4 | ((4 * t4 + i) << 4) | (hi2 << 8)] = (uint8_t)(w >> (8 * i));
             }
