@@ -321,6 +321,29 @@ def test_svdq_small(qt, M, K, N, r):
     assert_bf16_close(bf16_host(y), ref_y, "svdq y")
 
 
+@pytest.mark.parametrize("qt", [INT8, FP8])
+@pytest.mark.parametrize("K,r", [(256, 32), (1024, 16)])
+def test_svdq_multi_tile(qt, K, r):
+    """More 256x256 tiles (17 x 17, ragged) than CUs, so workgroups run several
+    tiles back to back (the low-rank operands of one tile's epilogue share the
+    stage ring with the next tile's loads); K = 256 gives single-group tiles."""
+    M, N = 4352 - 7, 4160 + 3
+    _say(f"svdq multi-tile qt={qt} M={M} K={K} N={N} r={r}")
+    rng = np.random.default_rng(K + r)
+    x = workloads.activations_bf16(rng, M, K, outliers=2)
+    l1 = workloads.normal_bf16(rng, (r, K), 0.1)
+    l2 = workloads.normal_bf16(rng, (N, r), 0.1)
+    res = workloads.normal_bf16(rng, (N, K), 0.02)
+    b = workloads.normal_bf16(rng, (N,), 0.02)
+    rq, _, sr = W8.w8a8_quant_weight_tensorwise(bf16_dev(res), qtype=qt)
+    y, xq, sx = W8.svdq_linear(bf16_dev(x), rq, sr, bf16_dev(l1), bf16_dev(l2), bf16_dev(b))
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([sample_rows(M, 6), [255, 256, M - 1]]))
+    orq, _, osr = oracle.quant_weight_tensorwise(qt, res)
+    ref_y, _, _ = oracle.svdq_linear(qt, x[rows], orq, osr, l1, l2, b)
+    assert_bf16_close(bf16_host(y)[rows], ref_y, "svdq y, several tiles per workgroup")
+
+
 def test_svdq_full_sampled():
     _say("svdq M4096 K3072 N12288 r32 sampled rows")
     d = workloads.svdq()

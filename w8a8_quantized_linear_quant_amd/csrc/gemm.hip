@@ -341,9 +341,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     // loads still allowed in flight when stage kt+1 must be complete: stages
     // kt+2 .. kt+NST-2 whole, and the parts of stage kt+NST-1 issued so far
     constexpr int kPending = (NST - 3) * kLoadsPerStage + (kParts - 1) * kPerPart;
-    auto run_stage = [&](auto sc, auto first_c) {
+    // defer (the low-rank epilogue only, last stage of a tile): this stage's
+    // refill -- the next tile's stage NST - 2 -- is issued after the epilogue
+    // instead, so that its buffer can hold the low-rank operands meanwhile.
+    auto run_stage = [&](auto sc, auto first_c, bool defer) {
         constexpr int S = decltype(sc)::value;
         constexpr bool FIRST = decltype(first_c)::value;
+        constexpr bool kMayDefer = EPI == kEpiLowRank32 && S == NST - 1;
+        const bool issue = !kMayDefer || !defer;
         uint8_t *cur = buf(sc);
         uint8_t *nxt = buf(std::integral_constant<int, (S + 1) % NST>{});
         uint8_t *refill = buf(std::integral_constant<int, (S + NST - 1) % NST>{});
@@ -354,18 +359,22 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                  if constexpr (kk + 1 < KSTEPS) {
                      __builtin_amdgcn_sched_barrier(0);
                      read_frags(cur, kk + 1, fa[P ^ 1], fb[P ^ 1]);
-                     load_part(refill, std::integral_constant<int, kk>{}, std::integral_constant<int, kParts>{});
+                     if (issue)
+                         load_part(refill, std::integral_constant<int, kk>{}, std::integral_constant<int, kParts>{});
                      mfmas(fa[P], fb[P], std::integral_constant<bool, FIRST && S == 0 && kk == 0>{});
                      interleave(std::integral_constant<int, kPerPart>{});
                      __builtin_amdgcn_sched_barrier(0);
                  } else {
-                     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPending) : "memory");
+                     // without this stage's earlier parts in flight, fewer may remain
+                     if (issue) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPending) : "memory");
+                     else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPending - (kParts - 1) * kPerPart) : "memory");
                      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
                      // a bare barrier: __syncthreads() would add a release fence,
                      // i.e. a wait for every load in flight, prefetches included
                      asm volatile("s_barrier" ::: "memory");
                      __builtin_amdgcn_sched_barrier(0);
-                     load_part(refill, std::integral_constant<int, kk>{}, std::integral_constant<int, kParts>{});
+                     if (issue)
+                         load_part(refill, std::integral_constant<int, kk>{}, std::integral_constant<int, kParts>{});
                      read_frags(nxt, 0, fa[P ^ 1], fb[P ^ 1]);
                      mfmas(fa[P], fb[P], std::integral_constant<bool, FIRST && S == 0 && kk == 0>{});
                      interleave(std::integral_constant<int, kPerPart>{});
@@ -374,14 +383,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
              }()),
              ...);
         }(std::make_integer_sequence<int, KSTEPS>{});
-        advance_cursor();
+        if (issue) advance_cursor();
     };
     static_assert(NST % 2 == 0 || KSTEPS % 2 == 0, "fragment parity must restart at each stage group");
     // stages FROM .. TO-1 of a group of NST
-    auto run_stages = [&](auto from_c, auto to_c, auto first_c) {
+    auto run_stages = [&](auto from_c, auto to_c, auto first_c, bool defer) {
         constexpr int F = decltype(from_c)::value, T = decltype(to_c)::value;
         [&]<int... S>(std::integer_sequence<int, S...>) {
-            (run_stage(std::integral_constant<int, F + S>{}, first_c), ...);
+            (run_stage(std::integral_constant<int, F + S>{}, first_c, defer), ...);
         }(std::make_integer_sequence<int, T - F>{});
     };
 
@@ -472,6 +481,41 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                 }
                 bias2[nb][j] = b;
             }
+        constexpr bool kLr32 = EPI == kEpiLowRank32;
+        uint8_t *ub = buf(std::integral_constant<int, NST - 1>{});
+        uint8_t *lb = buf(std::integral_constant<int, NST - 2>{});
+        const int half_bytes = 256 * p.rp * 2;
+        if constexpr (kLr32) {
+            // The low-rank operands of the workgroup's tile go to the two ring
+            // buffers that are free during the epilogue (the last stage's, and
+            // the one whose refill was deferred): u of its 256 rows (hi, then
+            // lo, [256][rp] bf16 each) and l2 of its 256 columns ([256][r],
+            // r == rp); every wave fetches a quarter of each.
+            {
+                const int n0 = nw - wn * 128;
+                const int cols_in = min(N - n0, 256);
+                const __amdgpu_buffer_rsrc_t rw2 = __builtin_amdgcn_make_buffer_rsrc(
+                    (void *)(p.l2 + (size_t)n0 * p.r), (short)0, cols_in * p.r * 2, kBufferRsrcWord3);
+                for (int i = 0; i < p.r / 8; ++i) {
+                    const int off = wave * 128 * p.r + i * 1024;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw2, (lds_ptr_t)(lb + off), 16, off + el * 16, 0, 0, 0);
+                }
+            }
+            const int m0 = mw - wm * 128;
+            const int rows_in = min(M - m0, 256);
+            const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(p.uhi + (size_t)m0 * p.rp), (short)0, rows_in * p.rp * 2, kBufferRsrcWord3);
+            const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(p.ulo + (size_t)m0 * p.rp), (short)0, rows_in * p.rp * 2, kBufferRsrcWord3);
+            for (int i = 0; i < p.rp / 8; ++i) {  // 128 rp bytes per wave and half, 1 KB per load
+                const int off = wave * 128 * p.rp + i * 1024;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_ptr_t)(ub + off), 16, off + el * 16, 0, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_ptr_t)(ub + half_bytes + off), 16, off + el * 16, 0,
+                                                         0, 0);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            asm volatile("s_barrier" ::: "memory");
+        }
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
@@ -480,6 +524,20 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
 #pragma unroll
                 for (int e = 0; e < 16; ++e) v[e] = (float)acc[nb][mb][e] * tm[mb];
                 if constexpr (EPI == kEpiLowRank) v = low_rank_add(p, v, nw + nb * 32, mw + mb * 32, erow, ehalf);
+                if constexpr (kLr32) {
+                    // u . l2^T of this block from the staged rows
+                    const int urow = wm * 128 + mb * 32 + erow, lrow2 = wn * 128 + nb * 32 + erow;
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks) {
+                        if (ks * 16 >= p.rp) break;
+                        const int j0 = ks * 16 + ehalf * 8;
+                        const v8bf a = *reinterpret_cast<const v8bf *>(lb + (lrow2 * p.r + j0) * 2);
+                        const v4u uh = *reinterpret_cast<const v4u *>(ub + (urow * p.rp + j0) * 2);
+                        const v4u ul = *reinterpret_cast<const v4u *>(ub + half_bytes + (urow * p.rp + j0) * 2);
+                        v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, uh), v, 0, 0, 0);
+                        v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, ul), v, 0, 0, 0);
+                    }
+                }
                 if constexpr (kCol) {
 #pragma unroll
                     for (int e = 0; e < 16; ++e) v[e] *= swc[nb][e / 4][e % 4];
@@ -536,13 +594,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         // The first NST stages start the accumulators (kt_end >= NST).  The
         // epilogue inputs are fetched before the second-to-last stage: the
         // waits at the ends of the last two stages cover them.
-        run_stages(std::integral_constant<int, 0>{}, std::integral_constant<int, NST>{}, std::true_type{});
+        run_stages(std::integral_constant<int, 0>{}, std::integral_constant<int, NST>{}, std::true_type{},
+                   kt_end == NST);
         for (int kt0 = NST; kt0 < kt_end; kt0 += NST) {
-            run_stages(std::integral_constant<int, 0>{}, std::integral_constant<int, NST - 2>{}, std::false_type{});
+            run_stages(std::integral_constant<int, 0>{}, std::integral_constant<int, NST - 2>{}, std::false_type{},
+                       false);
             if constexpr (kDma) {
                 if (interior && kt0 + NST == kt_end) epi_dma(mw, nw);
             }
-            run_stages(std::integral_constant<int, NST - 2>{}, std::integral_constant<int, NST>{}, std::false_type{});
+            run_stages(std::integral_constant<int, NST - 2>{}, std::integral_constant<int, NST>{}, std::false_type{},
+                       kt0 + NST == kt_end);
         }
         if constexpr (kDma) {
             if (interior && kt_end == NST) {
@@ -580,6 +641,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         } else {
             if (interior) bf16_epilogue(std::true_type{}, mw, nw);
             else bf16_epilogue(std::false_type{}, mw, nw);
+        }
+        // The staged u rows are read by every wave before any of them starts
+        // the next tile, whose first stage refills that buffer.
+        if constexpr (EPI == kEpiLowRank32) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            asm volatile("s_barrier" ::: "memory");
+            // the refill deferred from the tile's last stage: the next tile's
+            // stage NST - 2, into the buffer that held l2
+            load_part(buf(std::integral_constant<int, NST - 2>{}), std::integral_constant<int, 0>{},
+                      std::integral_constant<int, 1>{});
+            advance_cursor();
         }
         // The K loop counts VMEM operations in flight (vmcnt) on the premise
         // that they are all stage loads; let this tile's stores drain first.
@@ -631,11 +703,13 @@ w8a8_status gemm_launch(w8a8_qtype qtype, GemmEpilogue epi, const GemmArgs &a, h
         if (epi == kEpiI32) launch<W8A8_INT8, kEpiI32>(a, stream);
         else if (epi == kEpiBf16) launch<W8A8_INT8, kEpiBf16>(a, stream);
         else if (epi == kEpiLowRank) launch<W8A8_INT8, kEpiLowRank>(a, stream);
+        else if (epi == kEpiLowRank32) launch<W8A8_INT8, kEpiLowRank32>(a, stream);
         else launch<W8A8_INT8, kEpiColScale>(a, stream);
     } else {
         if (epi == kEpiI32) return W8A8_ERR_UNSUPPORTED;
         if (epi == kEpiBf16) launch<W8A8_FP8_E4M3, kEpiBf16>(a, stream);
         else if (epi == kEpiLowRank) launch<W8A8_FP8_E4M3, kEpiLowRank>(a, stream);
+        else if (epi == kEpiLowRank32) launch<W8A8_FP8_E4M3, kEpiLowRank32>(a, stream);
         else launch<W8A8_FP8_E4M3, kEpiColScale>(a, stream);
     }
     return launch_status();

@@ -12,6 +12,7 @@ enum GemmEpilogue {
     kEpiBf16 = 1,     // bf16(acc * sx[m] * sw + bias[n])
     kEpiLowRank = 2,  // bf16(acc * sx[m] * sw + u[m,:] . l2[n,:] + bias[n])
     kEpiColScale = 3, // bf16(acc * sx[m] * sw[n] + bias[n]), one weight scale per output channel
+    kEpiLowRank32 = 4, // as kEpiLowRank for r of 16 or 32, with u and l2 staged in LDS
 };
 
 struct GemmArgs {

@@ -136,5 +136,7 @@ extern "C" w8a8_status svdq_linear(w8a8_qtype qtype, const uint16_t *x, int64_t 
     a.l2 = l2;
     a.r = (int)r;
     a.rp = rp;
-    return gemm_launch(qtype, kEpiLowRank, a, stream);
+    // r of 16 or 32: the low-rank operands are staged in LDS (r == rp keeps
+    // the staged l2 rows aligned); other ranks read them from global memory
+    return gemm_launch(qtype, (r == 16 || r == 32) ? kEpiLowRank32 : kEpiLowRank, a, stream);
 }
