@@ -36,8 +36,9 @@
  *    Calls can therefore be captured into a HIP graph.  No global mutable
  *    state; calls on different streams with disjoint outputs may run
  *    concurrently.
- *  - All pointers must be 16-byte aligned (misaligned buffers were a known
- *    failure mode of the prior art: "offloading alignment 16").
+ *  - All pointers must be 16-byte aligned (OneTrainer PR #1034, "Known
+ *    issues", reports a misaligned-address failure that 16-byte alignment
+ *    fixed).
  *
  * Errors
  *  - Arguments are checked before anything is launched; on an error nothing
@@ -79,8 +80,9 @@ const char *w8a8_status_str(w8a8_status status);
 size_t w8a8_weight_workspace_bytes(int64_t N, int64_t K);
 
 /*
- * Tensor-wise weight quantization (wiki "Quantization": int W8A8 / float W8A8
- * "Tensor-wise quantization of weights").  One scale for all of W:
+ * Tensor-wise weight quantization (wiki "Quantization", int W8A8 / float W8A8
+ * "Technical": the weights get one scale for the whole tensor).  One scale
+ * for all of W:
  *   w_scale[0] = absmax scale of W;  wq[n, k] = code(W[n, k], w_scale).
  *   w      bf16 [N, K], contiguous.
  *   wq     codes [N, K], contiguous (int8 or e4m3 bytes).
@@ -101,9 +103,9 @@ w8a8_status w8a8_quant_weight_tensorwise(w8a8_qtype qtype, const uint16_t *w, in
 /* -------------------------------------------------------------- activations */
 
 /*
- * Row-wise (token-wise) activation quantization -- bitsandbytes' fused
- * "activation scale calibration and quantization" kernel (#1401, Enhancements)
- * applied to the W8A8 types of the OneTrainer wiki.  One pass over X:
+ * Row-wise (token-wise) activation quantization -- one kernel that both finds
+ * the row scales and quantizes, as bitsandbytes #1401 ("Enhancements") fused
+ * them, applied to the W8A8 types of the OneTrainer wiki.  One pass over X:
  *   x_scale[m] = absmax scale of row m;  xq[m, k] = code(X[m, k], x_scale[m]).
  *   x      bf16 [M, ldx]; the first K columns of each row are used.  The
  *          buffer spans M * ldx elements.
@@ -119,9 +121,9 @@ w8a8_status w8a8_quant_act_rowwise(w8a8_qtype qtype, const uint16_t *x, int64_t 
 /* --------------------------------------------------------------- the linear */
 
 /*
- * W8A8 linear (wiki "Quantization": "Linear layer matrix multiplications are
- * performed in int8" / "in float8") with the dequantization fused into the
- * product's epilogue:
+ * W8A8 linear (wiki "Quantization", int W8A8 / float W8A8 "Technical": the
+ * linear layer's matrix product runs in int8 or in float8) with the
+ * dequantization fused into the product's epilogue:
  *   acc[m, n] = sum_k xq[m, k] * wq[n, k]   (int32 exact, or f32 for e4m3)
  *   y[m, n]   = bf16(acc[m, n] * x_scale[m] * w_scale[0] + bias[n])
  *   xq [M, K] codes, x_scale f32 [M]; wq [N, K] codes, w_scale one f32;
@@ -134,8 +136,8 @@ w8a8_status w8a8_linear(w8a8_qtype qtype, const void *xq, const float *x_scale, 
                         uint16_t *y, hipStream_t stream);
 
 /*
- * Input gradient of the W8A8 linear with frozen W ("Activations are quantized
- * token-wise during training"): dX = dY . W, from dY quantized row-wise
+ * Input gradient of the W8A8 linear with frozen W (the wiki quantizes the
+ * activations token-wise in training too): dX = dY . W, from dY quantized row-wise
  * (dyq [M, N], dy_scale f32 [M]) and the transposed weight codes produced by
  * w8a8_quant_weight_tensorwise (wq_t [K, N], w_scale):
  *   dx[m, k] = bf16(sum_n dyq[m, n] * wq_t[k, n] * dy_scale[m] * w_scale[0]).
@@ -210,7 +212,8 @@ w8a8_status svdq_prepare(const uint16_t *w, int64_t N, int64_t K, int64_t r, con
 /* -------------------------------------------------------------------- Q8_0 */
 
 /* Size in bytes of n values in GGUF Q8_0 blocks: 34 * ceil(n / 32) (struct
- * Q8_0: "32 values -> 34 bytes (2 scale + 32 data)").  Returns 0 for n < 0. */
+ * Q8_0: each block holds 32 values in 34 bytes, a 2-byte scale then 32 codes).
+ * Returns 0 for n < 0. */
 size_t q8_0_nbytes(int64_t n);
 
 /*

@@ -4,7 +4,7 @@ Only the tests (and the benchmark's CPU-baseline leg) may import this module;
 the product library never calls it.
 
 OneTrainer PR #1034 "SVDQuant" and the wiki's SVDQuant entry: the weight is
-split into a bf16 low-rank pair (rank 16-32 is enough) plus a residual that is
+split into a bf16 low-rank pair (of rank 16 to 32) plus a residual that is
 quantized like any W8A8 weight.  The pages name the method only by its paper;
 the split computed here is the plainest one that agrees with them:
 

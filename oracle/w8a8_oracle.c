@@ -24,8 +24,8 @@
  *  - fp8 means OCP E4M3FN (max finite 448, no infinities), QMAX = 448, and the
  *    quotient is clamped to [-448, 448] before it is rounded to e4m3;
  *  - Q8_0 codes are computed from the f32 scale; the stored block scale is
- *    f16(scale) ("stored as f32, converted to f16 on export"); dequantize uses
- *    the stored f16 scale;
+ *    f16(scale) (the page keeps f32 scales and converts them to f16 when it
+ *    writes the GGUF blocks); dequantize uses the stored f16 scale;
  *  - the dequantized linear output is bf16(acc * sx[m] * sw + bias[n]) with the
  *    right-hand side evaluated in double and rounded to bf16 once;
  *  - the SVDQuant branch adds (X . L1^T) . L2^T, both products in double;
@@ -46,7 +46,7 @@
 
 /* ------------------------------------------------------------------------- */
 /* Number formats.  Each format is decoded by its definition; encoding to it is */
-/* "pick the nearest representable value, ties to the even code", found by a    */
+/* the nearest representable value, ties going to the even code, found by a     */
 /* binary search over the monotone code space and a comparison with the exact   */
 /* midpoint (which double holds exactly for all three formats).                 */
 /* ------------------------------------------------------------------------- */

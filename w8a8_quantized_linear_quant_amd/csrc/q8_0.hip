@@ -4,7 +4,7 @@
 // block, 34 bytes: 2-byte f16 scale + 32 int8 codes), Q8_0::quantize (block
 // absmax, scale = absmax / 127 floored at 1e-10, value / scale rounded and
 // clamped to [-128, 127], zero padding of the partial last block; the f32
-// scale is converted to f16 on export) and Q8_0::dequantize (code * scale,
+// scale becomes f16 when the blocks are written) and Q8_0::dequantize (code * scale,
 // here with the stored f16 scale).
 //
 // Both kernels stream: 8 lanes own one 32-value block (4 values = 16 bytes of
