@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw8a8.so")
 OBJDIR = os.path.join(HERE, "_build")
 SOURCES = ["act_quant.hip", "weight_quant.hip", "gemm.hip", "svdq.hip", "q8_0.hip", "gguf_a8.hip", "svd_prep.hip", "hadamard.hip", "status.cpp"]
-HEADERS = ["common.hpp", "internal.hpp"]
+HEADERS = ["common.hpp", "internal.hpp", "act_quant.hpp"]  # shared by the sources above
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
