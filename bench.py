@@ -104,6 +104,24 @@ def _traffic_from_profile(kernel_hash):
         return None
 
 
+def measured_peaks(w8, torch, a_codes, b_codes):
+    """Ceilings measured on this GPU: the sustained int8 MFMA rate on fragments
+    of the given codes (TOPS) and the bandwidth of a plain device copy (GB/s)."""
+    pairs = 16384                       # ~10 ms per probe launch
+    cus = w8.library().w8a8_probe_sink_count() // 256
+    ops = pairs * 32 * 2 * 32 ** 3 * 4 * cus
+    sink = w8.probe_mfma_i8(a_codes, b_codes, pairs)
+    w8.probe_mfma_i8(a_codes, b_codes, pairs, sink=sink)
+    ms = _time_launches(lambda i: w8.probe_mfma_i8(a_codes, b_codes, pairs, sink=sink), 3, 1)
+    mfma_tops = ops / (ms * 1e-3) / 1e12
+    src = torch.empty(1 << 29, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    ms_copy = _time_launches(lambda i: dst.copy_(src), 5, 2)
+    copy_gbs = 2.0 * src.numel() / (ms_copy * 1e-3) / 1e9
+    del src, dst
+    return round(mfma_tops, 1), round(copy_gbs, 1)
+
+
 def cpu_baseline(x_bits, w_bits, b_bits, rows):
     """The oracle (plain C, one thread) on the first `rows` rows of the same
     workload: act-quant + weight quant + linear, scaled to TOPS of the linear."""
@@ -206,6 +224,13 @@ def main():
            "frac": round(aq_gbs / PEAK_HBM_GBS, 4), "us_per_launch": round(ms_aq * 1e3, 2),
            "algorithmic_bytes_per_launch": aq_bytes, "kernel": "act_quant_rowwise_kernel<int8>",
            "launches": AQ_ITERS, "buffer_sets": AQ_ROTATE}
+    # the same rates against ceilings measured here, in the same power state
+    mfma_tops, copy_gbs = measured_peaks(w8, torch, sets[0]["xq"], sets[0]["wq"])
+    roofline.update(measured_peak=mfma_tops, frac_of_measured_peak=round(gemm_tops / mfma_tops, 4),
+                    measured_peak_how="int8 MFMA loop (v_mfma_i32_32x32x32_i8, one wave per SIMD, all CUs) "
+                                      "on fragments of this step's activation and weight codes")
+    act.update(measured_peak=copy_gbs, frac_of_measured_peak=round(aq_gbs / copy_gbs, 4),
+               measured_peak_how="device-to-device copy of 512 MiB, read + write bytes")
 
     if args.calibrate_copy:
         src = torch.empty(1 << 29, dtype=torch.uint8, device="cuda").fill_(1)

@@ -17,8 +17,17 @@ NULL = None
 def test_exports_match_header():
     names = w8.exported_names_in_header()
     assert len(names) == 19
-    for n in names:
+    probe = w8.exported_names_in_header(w8.PROBE_HEADER)
+    assert probe == ["w8a8_probe_mfma_i8", "w8a8_probe_sink_count"]
+    for n in names + probe:
         assert hasattr(lib, n), n
+
+
+def test_probe_rejects():
+    assert lib.w8a8_probe_mfma_i8(NULL, A, 1, A, NULL) == INVALID
+    assert lib.w8a8_probe_mfma_i8(A, A, -1, A, NULL) == INVALID
+    assert lib.w8a8_probe_mfma_i8(MIS, A, 1, A, NULL) == ALIGN
+    assert lib.w8a8_probe_mfma_i8(A, A, 0, A, NULL) == OK
 
 
 def test_status_strings():

@@ -656,3 +656,18 @@ def test_determinism_and_graph_capture():
         _ = (x.float() * 2).sum()  # unrelated eager work between replays
         torch.cuda.synchronize()
     del d
+
+
+# ------------------------------------------------------------ diagnostics
+def test_probe_mfma_runs():
+    _say("probe mfma i8")
+    z = torch.zeros(65536, dtype=torch.int8, device="cuda")
+    sink = W8.probe_mfma_i8(z, z, 4)
+    torch.cuda.synchronize()
+    assert sink.numel() == W8.library().w8a8_probe_sink_count()
+    assert not sink.any()                      # zero operands accumulate zeros
+    r = torch.randint(-128, 128, (65536,), dtype=torch.int8, device="cuda")
+    s1 = W8.probe_mfma_i8(r, r, 4).clone()
+    s2 = W8.probe_mfma_i8(r, r, 4)
+    torch.cuda.synchronize()
+    assert torch.equal(s1, s2) and s1.any()    # deterministic, not optimized away

@@ -16,6 +16,7 @@ the current stream.  The functions carry the C names:
   q8_0_quantize / q8_0_dequantize / q8_0_nbytes   GGUF Q8_0 blocks
   gguf_a8_requant_q8_0          Q8_0 weight -> int8 / e4m3 codes, one scale per output channel
   gguf_a8_linear                8-bit product with per-channel weight scales -> bf16
+  probe_mfma_i8                 diagnostic: sustained int8 MFMA loop (include/w8a8_probe.h)
 
 Codes are torch.int8 (int8) or torch.float8_e4m3fn (e4m3); bf16 tensors are
 torch.bfloat16; scales are float32.  Output tensors may be passed in (`out=`)
@@ -35,6 +36,7 @@ FP8_E4M3 = 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "w8a8.h")
+PROBE_HEADER = os.path.join(os.path.dirname(_HERE), "include", "w8a8_probe.h")
 
 
 class W8A8Error(RuntimeError):
@@ -68,6 +70,8 @@ def _load_library():
         "svdq_prepare": (I, [P, I64, I64, I64, P, I, P, P, P, P, P, P]),
         "w8a8_quant_act_rowwise_hadamard": (I, [I, P, I64, I64, I64, P, I64, P, P]),
         "w8a8_hadamard_rotate": (I, [P, I64, I64, I64, P, I64, P]),
+        "w8a8_probe_sink_count": (I64, []),
+        "w8a8_probe_mfma_i8": (I, [P, P, I64, P, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -344,3 +348,20 @@ def gguf_a8_linear(xq, x_scale, wq, w_scale, bias=None, out=None):
     _check(_lib.gguf_a8_linear(qt, _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(bias), M, N, K, _ptr(y),
                                _stream(xq.device)))
     return y
+
+
+# ---------------------------------------------------------------- diagnostics
+def probe_mfma_i8(a, b, pairs, sink=None):
+    """Sustained int8 MFMA loop on operand bytes `a`, `b` (device tensors of at
+    least 65536 bytes each): `pairs` iterations of 32 products per wave, one
+    workgroup of 4 waves per CU.  Returns the sink tensor; the integer
+    operations are pairs * 32 * 2 * 32**3 * 4 * CUs."""
+    import torch
+    for t in (a, b):
+        if t.numel() * t.element_size() < 65536 or not t.is_contiguous():
+            raise ValueError("probe operands: contiguous, at least 65536 bytes")
+    n = _lib.w8a8_probe_sink_count()
+    if sink is None:
+        sink = torch.empty(n, dtype=torch.int32, device=a.device)
+    _check(_lib.w8a8_probe_mfma_i8(_ptr(a), _ptr(b), int(pairs), _ptr(sink), _stream(a.device)))
+    return sink

@@ -13,7 +13,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw8a8.so")
 OBJDIR = os.path.join(HERE, "_build")
-SOURCES = ["act_quant.hip", "weight_quant.hip", "gemm.hip", "svdq.hip", "q8_0.hip", "gguf_a8.hip", "svd_prep.hip", "hadamard.hip", "status.cpp"]
+SOURCES = ["act_quant.hip", "weight_quant.hip", "gemm.hip", "svdq.hip", "q8_0.hip", "gguf_a8.hip", "svd_prep.hip", "hadamard.hip", "probe.hip",
+           "status.cpp"]
 HEADERS = ["common.hpp", "internal.hpp", "act_quant.hpp"]  # shared by the sources above
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
