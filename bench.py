@@ -203,6 +203,9 @@ def main():
     # kernel on its own input sets, enough of them that each launch reads cold HBM
     iters = max(args.steps, 20)
     ms_gemm = _time_launches(gemm, iters, 100)
+    each = np.array(_time_each(gemm, iters)) * 1e3
+    spread = {"us_p10": round(float(np.percentile(each, 10)), 2), "us_median": round(float(np.median(each)), 2),
+              "us_p90": round(float(np.percentile(each, 90)), 2)}
     aq_sets = [(sets[0]["x"].clone(), torch.empty((M, K), dtype=torch.int8, device="cuda"),
                 torch.empty(M, dtype=torch.float32, device="cuda")) for _ in range(AQ_ROTATE)]
 
@@ -219,7 +222,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
                 "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": _traffic_from_profile(khash),
                 "kernel": "gemm_kernel<int8, bf16 epilogue>", "us_per_launch": round(ms_gemm * 1e3, 2),
-                "algorithmic_ops_per_launch": ops, "kernel_source_hash": khash}
+                "algorithmic_ops_per_launch": ops, "kernel_source_hash": khash, **spread}
     act = {"bound": "hbm", "achieved": round(aq_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
            "frac": round(aq_gbs / PEAK_HBM_GBS, 4), "us_per_launch": round(ms_aq * 1e3, 2),
            "algorithmic_bytes_per_launch": aq_bytes, "kernel": "act_quant_rowwise_kernel<int8>",
@@ -264,6 +267,18 @@ def main():
         "rows": rows,
     }
     print(json.dumps(out), flush=True)
+
+
+def _time_each(fn, iters):
+    """Per-launch durations (ms) of fn(i), an event pair around every launch."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i, (a, b) in enumerate(ev):
+        a.record()
+        fn(i)
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
 
 
 def _time_row(fn, settle_ms=30.0, span_ms=30.0):
