@@ -129,7 +129,9 @@ w8a8_status w8a8_quant_act_rowwise(w8a8_qtype qtype, const uint16_t *x, int64_t 
  *   xq [M, K] codes, x_scale f32 [M]; wq [N, K] codes, w_scale one f32;
  *   bias bf16 [N] or NULL; y bf16 [M, N].
  * Shape rules: M, N >= 0; K >= 16, K % 16 == 0 (pad K with zero codes: a zero
- * code adds exactly 0).  Any M and N, including ragged tile tails.
+ * code adds exactly 0).  Any M and N, including ragged tile tails.  The int32
+ * sum is exact while |acc| < 2^31: always for codes the quantizers produce
+ * (|q| <= 127) when K <= 133143, since 127^2 K < 2^31.
  */
 w8a8_status w8a8_linear(w8a8_qtype qtype, const void *xq, const float *x_scale, const void *wq,
                         const float *w_scale, const uint16_t *bias, int64_t M, int64_t N, int64_t K,

@@ -162,6 +162,22 @@ def test_gemm_i32_extremes():
     assert_equal(acc.cpu().numpy(), oracle.gemm_i32(a, b), "extremes")
 
 
+def test_gemm_i32_longest_exact_k():
+    """K = 131072 with codes at +-127 (the quantizers' range): |acc| reaches
+    127^2 K = 2,114,060,288, just below 2^31, and must stay exact."""
+    K = 131072
+    a = np.full((3, K), 127, np.int8)
+    a[1] = -127
+    a[2, 1::2] = -127
+    b = np.full((2, K), 127, np.int8)
+    b[1, ::3] = -127
+    acc = W8.w8a8_gemm_i32(codes_dev(a, False), codes_dev(b, False))
+    torch.cuda.synchronize()
+    ref = oracle.gemm_i32(a, b)
+    assert abs(int(ref[0, 0])) == 127 * 127 * K
+    assert_equal(acc.cpu().numpy(), ref, "int32 accumulators at the longest exact K")
+
+
 def test_gemm_i32_full_size_sampled():
     _say("gemm_i32 M4096 N12288 K3072 sampled rows")
     rng = np.random.default_rng(11)
