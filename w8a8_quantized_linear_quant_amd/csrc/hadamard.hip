@@ -18,8 +18,9 @@
 // keeps the whole row in registers: each lane loads 16 consecutive values of
 // each block (stages h = 1..8 in registers), one LDS transpose regroups the
 // block so that element bits 4-7 are in registers (h = 16..128) and bits 8-9
-// are lane bits 0-1 (h = 256, 512 through DPP quad permutes), then the codes
-// go back through LDS to leave as one 16-byte store per lane and block.
+// are lane bits 4-5 (h = 256, 512: a row swap between register pairs,
+// v_permlane16/32_swap, makes each of these butterflies lane-local), then the
+// codes go back through LDS to leave as one 16-byte store per lane and block.
 // Other block sizes use a per-wave LDS transform (two passes over the row).
 // Weights: the same transform, rounded to bf16 (one-time).
 #include "internal.hpp"
@@ -72,12 +73,20 @@ __device__ __forceinline__ void zero_pad_row(uint8_t *qrow, int64_t K, int64_t l
 __device__ __forceinline__ int pad_pos(int e) { return e + 16 * (e >> 8); }
 constexpr int kPadBlockFloats = 1024 + 16 * 4;
 
-// Butterfly across lanes l and l ^ m (m = 1 or 2) with a DPP quad permute:
-// the lane whose bit is clear keeps a + d, the other d' - a' = a - d.
-template <int CTRL>
-__device__ __forceinline__ float xlane_butterfly(float v, float sgn) {
-    const float p = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-    return __builtin_fmaf(sgn, v, p);
+// Butterflies of a stage whose element bit is lane bit 4 (W = 16) or 5
+// (W = 32), on the register pair (x, y): v_permlane{16,32}_swap exchanges the
+// W-lane rows of x that have that lane bit set with the rows of y that have it
+// clear.  Afterwards every lane holds in (x, y) two values whose elements
+// differ in the stage's bit alone (the one with the bit clear in x), from x's
+// elements where the lane bit is clear and from y's where it is set; the
+// butterfly is then the same in every lane: x <- x + y, y <- x - y.
+template <int W>
+__device__ __forceinline__ void swap_butterfly(float &x, float &y) {
+    const auto p = W == 16 ? __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false)
+                           : __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    const float a = __uint_as_float(p[0]), d = __uint_as_float(p[1]);
+    x = a + d;
+    y = a - d;
 }
 
 template <int QT, int NB>  // NB blocks of 1024 per row
@@ -90,9 +99,12 @@ __global__ __launch_bounds__(kThreads) void hadamard_act_quant_1024_kernel(const
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     float *sb = lds[wave];
-    // layout B: lane l' holds e = ((l' >> 2) & 15) | (t' << 4) | ((l' & 3) << 8), t' = 0..15
-    const int lo4 = (lane >> 2) & 15, hi2 = lane & 3;
-    const float sgn1 = (lane & 1) ? -1.0f : 1.0f, sgn2 = (lane & 2) ? -1.0f : 1.0f;
+    // layout B: lane l holds e = (l & 15) | (t << 4) | ((l >> 4) << 8), t = 0..15
+    const int lo4 = lane & 15, hi2 = lane >> 4;
+    // Final layout, after the swaps of stages h = 256 and 512: lane l, value i
+    // is element ((l & 31) | ((i >> 2) << 5) | ((l >> 5) << 7) |
+    // (((i >> 1) & 1) << 8) | ((i & 1) << 9)); byte offset of i = 0:
+    const int fin = (lane & 31) | ((lane >> 5) << 7);
     const float c = 1.0f / 32.0f;  // 1 / sqrt(1024), exact
     const int64_t stride = (int64_t)gridDim.x * kRowsPerBlock;
 
@@ -141,14 +153,21 @@ __global__ __launch_bounds__(kThreads) void hadamard_act_quant_1024_kernel(const
                         u[t] = a + dd;
                         u[t + h] = a - dd;
                     }
-            // stages h = 256, 512 (lane bits 0, 1)
+            // stage h = 256 (lane bit 4) on the pairs (2j, 2j + 1): then lane
+            // l, value 2j + s holds element (l & 15) | ((2j + l4) << 4) |
+            // (s << 8) | (l5 << 9), with l4, l5 lane bits 4 and 5
 #pragma unroll
-            for (int t = 0; t < 16; ++t) u[t] = xlane_butterfly<0xB1>(u[t], sgn1);  // quad_perm [1,0,3,2]
+            for (int j = 0; j < 8; ++j) swap_butterfly<16>(u[2 * j], u[2 * j + 1]);
+            // stage h = 512 (lane bit 5) on the pairs (k, k + 8), into the
+            // final layout: value 2k + s2 from pair k, s2 = element bit 9
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                vb[blk][t] = xlane_butterfly<0x4E>(u[t], sgn2);  // quad_perm [2,3,0,1]
-                amax = fmaxf(amax, fabsf(vb[blk][t]));
+            for (int k = 0; k < 8; ++k) {
+                swap_butterfly<32>(u[k], u[k + 8]);
+                vb[blk][2 * k] = u[k];
+                vb[blk][2 * k + 1] = u[k + 8];
             }
+#pragma unroll
+            for (int t = 0; t < 16; ++t) amax = fmaxf(amax, fabsf(vb[blk][t]));
         }
         // The scale c = 2^-5 is exact, so it moves from the values to the
         // divisor: scale from f32(amax c), codes from v / (32 s) with
@@ -162,12 +181,12 @@ __global__ __launch_bounds__(kThreads) void hadamard_act_quant_1024_kernel(const
         uint8_t *cb = reinterpret_cast<uint8_t *>(sb);  // 1 KB of codes per block
 #pragma unroll
         for (int blk = 0; blk < NB; ++blk) {
-            // codes in layout B -> bytes at their element positions in LDS
+            // codes in the final layout -> bytes at their element positions
 #pragma unroll
             for (int t4 = 0; t4 < 4; ++t4) {
                 const uint32_t w = codes4<QT>(&vb[blk][4 * t4], s32, r32);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) cb[lo4 | ((4 * t4 + i) << 4) | (hi2 << 8)] = (uint8_t)(w >> (8 * i));
+                for (int i = 0; i < 4; ++i) cb[fin | (t4 << 5) | (((i >> 1) & 1) << 8) | ((i & 1) << 9)] = (uint8_t)(w >> (8 * i));
             }
             // layout A out: 16 contiguous codes per lane
             const v4u out = *reinterpret_cast<const v4u *>(cb + 16 * lane);
