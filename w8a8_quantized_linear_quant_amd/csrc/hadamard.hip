@@ -184,9 +184,18 @@ __global__ __launch_bounds__(kThreads) void hadamard_act_quant_1024_kernel(const
             // codes in the final layout -> bytes at their element positions
 #pragma unroll
             for (int t4 = 0; t4 < 4; ++t4) {
-                const uint32_t w = codes4<QT>(&vb[blk][4 * t4], s32, r32);
+                if constexpr (QT == W8A8_INT8) {
+                    // the code is the low byte of the magic-add result
 #pragma unroll
-                for (int i = 0; i < 4; ++i) cb[fin | (t4 << 5) | (((i >> 1) & 1) << 8) | ((i & 1) << 9)] = (uint8_t)(w >> (8 * i));
+                    for (int i = 0; i < 4; ++i)
+                        cb[fin | (t4 << 5) | (((i >> 1) & 1) << 8) | ((i & 1) << 9)] =
+                            (uint8_t)__float_as_uint(quotient_nosign(vb[blk][4 * t4 + i], s32, r32) + 12582912.0f);
+                } else {
+                    const uint32_t w = codes4<QT>(&vb[blk][4 * t4], s32, r32);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        cb[fin | (t4 << 5) | (((i >> 1) & 1) << 8) | ((i & 1) << 9)] = (uint8_t)(w >> (8 * i));
+                }
             }
             // layout A out: 16 contiguous codes per lane
             const v4u out = *reinterpret_cast<const v4u *>(cb + 16 * lane);
