@@ -51,22 +51,29 @@ __global__ __launch_bounds__(kThreads) void gguf_a8_requant_row_kernel(const uin
         const uint32_t a0 = s0 & ~15u;
         const int off = (int)(s0 - a0);
         const int nvec = (off + (int)row_bytes + 15) / 16;
-        for (int i = lane; i < nvec; i += 64) {
-            const uint32_t vo = a0 + 16u * i;
-            v4u v;
-            if (vo + 16u <= total_bytes) {
-                v = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, vo, 0, 0));
-            } else {
-                // the tensor's last 16 bytes run past its end: a wide load
-                // that crosses num_records reads zero as a whole, so take the
-                // remaining bytes one by one
-                uint8_t t[16];
+        // Stage the row: every lane issues 4 loads before it writes any of
+        // them to LDS (vector indices past the row are clamped to its last
+        // vector: a repeated load whose data is dropped).
+        for (int i0 = 0; i0 < nvec; i0 += 256) {
+            v4u t[4];
 #pragma unroll
-                for (int j = 0; j < 16; ++j) t[j] = __builtin_amdgcn_raw_buffer_load_b8(rs, vo + j, 0, 0);
-                v = __builtin_bit_cast(v4u, t);
+            for (int j = 0; j < 4; ++j) {
+                const int i = min(i0 + lane + 64 * j, nvec - 1);
+                t[j] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rs, a0 + 16u * i, 0, 0));
             }
-            *reinterpret_cast<v4u *>(st + 16 * i) = v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = i0 + lane + 64 * j;
+                if (i < nvec) *reinterpret_cast<v4u *>(st + 16 * i) = t[j];
+            }
         }
+        // The tensor's last 16 bytes may run past its end: a wide load that
+        // crosses num_records reads zero as a whole, so that vector is read
+        // again byte by byte (bytes past the end read zero).  Same wave, so
+        // these LDS writes land after the ones above.
+        const uint32_t vlast = a0 + 16u * (nvec - 1);
+        if (vlast + 16u > total_bytes && lane < 16)
+            st[16 * (nvec - 1) + lane] = __builtin_amdgcn_raw_buffer_load_b8(rs, vlast + lane, 0, 0);
         // values of this lane's 4 codes of block b (b < nb)
         auto block_vals = [&](int b, float *v) {
             const uint8_t *bp = st + off + b * 34;
@@ -78,49 +85,65 @@ __global__ __launch_bounds__(kThreads) void gguf_a8_requant_row_kernel(const uin
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[i] = (float)(int8_t)(w >> (8 * i)) * d;  // exact in f32
         };
-        // row absmax (non-negative floats order like their bit patterns)
+        // Row absmax (non-negative floats order like their bit patterns), 32
+        // blocks (4 steps of 8) per iteration with their LDS reads issued
+        // together; block indices past the row repeat its last block.
         uint32_t amax_bits = 0;
-        for (int b0 = 0; b0 < nb; b0 += 8) {
-            const int b = b0 + blk_in_step;
-            if (b < nb) {
-                float v[4];
-                block_vals(b, v);
-                const float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+        for (int b0 = 0; b0 < nb; b0 += 32) {
+            float v[4][4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) block_vals(min(b0 + 8 * q + blk_in_step, nb - 1), v[q]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float a = fmaxf(fmaxf(fabsf(v[q][0]), fabsf(v[q][1])), fmaxf(fabsf(v[q][2]), fabsf(v[q][3])));
                 amax_bits = max(amax_bits, __float_as_uint(a));
             }
         }
         const float s = absmax_scale(__uint_as_float(wave_max_u32(amax_bits)), qmax);
         const float r = 1.0f / s;
         if (lane == 0) scale[n] = s;
-        // codes, in place: the reads of a step (blocks b0..b0+7 at >= 34 b0)
-        // precede its writes (32 b0 .. 32 b0 + 255) in the wave's LDS order,
-        // and later steps read from 34 (b0 + 8) > 32 b0 + 255 on
-        for (int b0 = 0; b0 < nb; b0 += 8) {
-            const int b = b0 + blk_in_step;
-            if (b < nb) {
-                float v[4];
-                block_vals(b, v);
+        // Codes, in place: the reads of an iteration (blocks b0..b0+31, bytes
+        // from off + 34 b0 on) precede its writes (32 b0 .. 32 b0 + 1023) in
+        // the wave's LDS order, and later iterations read from
+        // 34 (b0 + 32) > 32 b0 + 1023 on.
+        for (int b0 = 0; b0 < nb; b0 += 32) {
+            float v[4][4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) block_vals(min(b0 + 8 * q + blk_in_step, nb - 1), v[q]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int b = b0 + 8 * q + blk_in_step;
                 uint32_t word = 0;
                 if constexpr (QT == W8A8_INT8) {
                     // |v / s| <= 127 by the scale rule: no clamp needed; the
                     // add of 1.5 * 2^23 rounds half to even
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
-                        word |= (__float_as_uint(quotient_nosign(v[i], s, r) + 12582912.0f) & 0xFFu) << (8 * i);
+                        word |= (__float_as_uint(quotient_nosign(v[q][i], s, r) + 12582912.0f) & 0xFFu) << (8 * i);
                 } else {
-                    float q[4];
+                    float c[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) q[i] = __builtin_amdgcn_fmed3f(quotient(v[i], s, r), -448.0f, 448.0f);
-                    int pk = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
-                    pk = __builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], pk, true);
+                    for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_fmed3f(quotient(v[q][i], s, r), -448.0f, 448.0f);
+                    int pk = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+                    pk = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], pk, true);
                     word = (uint32_t)pk;
                 }
-                *reinterpret_cast<uint32_t *>(st + b * 32 + 4 * part) = word;
+                if (b < nb) *reinterpret_cast<uint32_t *>(st + b * 32 + 4 * part) = word;
             }
         }
+        // the row's codes leave as 16-byte stores, 4 LDS reads per lane at a time
         uint8_t *orow = wq + (size_t)n * K;
-        for (int i = lane; i < K / 16; i += 64)
-            *reinterpret_cast<v4u *>(orow + 16 * i) = *reinterpret_cast<const v4u *>(st + 16 * i);
+        const int nout = K / 16;
+        for (int i0 = 0; i0 < nout; i0 += 256) {
+            v4u t[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) t[j] = *reinterpret_cast<const v4u *>(st + 16 * min(i0 + lane + 64 * j, nout - 1));
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = i0 + lane + 64 * j;
+                if (i < nout) *reinterpret_cast<v4u *>(orow + 16 * i) = t[j];
+            }
+        }
     }
 }
 
