@@ -23,11 +23,18 @@ constexpr int kBlocksPerWave = 8;
 constexpr int kGroupBytes = kBlocksPerWave * kBlockBytes;  // 272
 constexpr int kUnroll = 4;                                 // wave groups per iteration
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_max(float v) {
+    return fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false)));
+}
+
 __device__ __forceinline__ float group8_max(float v) {
-    // max over the 8 lanes of one block (lanes 8b .. 8b+7)
-#pragma unroll
-    for (int off = 1; off < 8; off <<= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
+    // max over the 8 lanes of one block (lanes 8b .. 8b+7), in DPP: lane ^ 1,
+    // lane ^ 2 (quad permutes), then the mirror within 8 lanes, which pairs
+    // every lane with one of the other quad
+    v = dpp_max<0xB1>(v);   // quad_perm [1,0,3,2]
+    v = dpp_max<0x4E>(v);   // quad_perm [2,3,0,1]
+    return dpp_max<0x141>(v);  // row_half_mirror
 }
 
 __global__ __launch_bounds__(kThreads) void q8_0_quantize_kernel(const float *__restrict__ x, int64_t n,
