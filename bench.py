@@ -137,7 +137,19 @@ def cpu_baseline(x_bits, w_bits, b_bits, rows):
     return {"value": round(ops / (t2 - t1) / 1e12, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
             "sample": f"first {rows} of {M} rows: act-quant + int8 linear ({rows}x{N}x{K}); "
                       f"weight quant ({N}x{K}) timed apart: {t1 - t0:.2f} s",
-            "seconds": round(t2 - t1, 2)}
+            "seconds": round(t2 - t1, 2), "host_cpu": _host_cpu(), "host_threads": os.cpu_count()}
+
+
+def _host_cpu():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def main():
