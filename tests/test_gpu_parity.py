@@ -239,6 +239,28 @@ def test_linear_dit_sampled(which):
     assert_bf16_close(got[rows], oracle.linear(INT8, xq, sx, wq, sw, b), f"dit {which}")
 
 
+def test_linear_headline_full_sampled():
+    """The timed step itself: X [4096, 3072] with outlier channels, W [12288,
+    3072], bias, int8 -- the inputs and the launches the benchmark times
+    (act-quant, then the product with the bf16 epilogue), on sampled rows:
+    codes and row scales bit for bit, Y within the bf16 bound."""
+    _say("linear headline M4096 K3072 N12288 int8 sampled rows")
+    d = workloads.svdq()
+    x, w, b = d["x"], d["r"], d["bias"]
+    xq, sx = W8.w8a8_quant_act_rowwise(bf16_dev(x))
+    wq, _, sw = W8.w8a8_quant_weight_tensorwise(bf16_dev(w))
+    y = W8.w8a8_linear(xq, sx, wq, sw, bf16_dev(b))
+    torch.cuda.synchronize()
+    rows = sample_rows(x.shape[0], 8)
+    rxq, rsx = oracle.quant_act_rowwise(INT8, x[rows])
+    rwq, _, rsw = oracle.quant_weight_tensorwise(INT8, w)
+    assert_equal(sx.cpu().numpy()[rows].view(np.uint32), rsx.view(np.uint32), "row scales")
+    assert_equal(bytes_host(xq)[rows], rxq, "activation codes")
+    assert_equal(sw.cpu().numpy().reshape(-1).view(np.uint32),
+                 np.atleast_1d(np.float32(rsw)).view(np.uint32), "weight scale")
+    assert_bf16_close(bf16_host(y)[rows], oracle.linear(INT8, rxq, rsx, rwq, rsw, b), "headline Y")
+
+
 def test_fp8_exact_on_small_integer_codes():
     # codes of {0, +-1, +-2, +-4} with unit scales: every f32 partial sum is
     # exact, so the bf16 output must match bit for bit.
