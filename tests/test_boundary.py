@@ -114,6 +114,8 @@ def test_binding_refuses_cpu_tensors():
         w8.w8a8_quant_act_rowwise(x)
     with pytest.raises(TypeError):
         w8.w8a8_quant_act_rowwise(x.float())
+    with pytest.raises(ValueError):                      # neither INT8 nor FP8_E4M3
+        w8.w8a8_quant_weight_tensorwise(x, qtype=5)
 
 
 def test_gguf_a8_rejects():

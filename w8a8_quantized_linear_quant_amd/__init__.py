@@ -117,14 +117,65 @@ def _qtype_of(codes):
 
 
 def _code_dtype(qtype):
+    if qtype not in (INT8, FP8_E4M3):
+        raise ValueError(f"qtype must be INT8 ({INT8}) or FP8_E4M3 ({FP8_E4M3}), got {qtype}")
     return torch.int8 if qtype == INT8 else torch.float8_e4m3fn
 
 
 def _need(t, dtype, name):
-    if t.dtype != dtype:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
+
+
+def _arg(t, dtype, name, device, min_numel=0):
+    """An input tensor: dtype (None: any), on `device`, at least `min_numel`
+    elements; returned contiguous (a copy only if it was not)."""
+    _need(t, dtype, name)
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the other operands on {device}")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs at least {min_numel}")
+    return t.contiguous()
+
+
+def _out(t, shape, dtype, device, name):
+    """An output of exactly `shape`: allocated if None, else checked (dtype,
+    device, shape, contiguous): the kernels write every element of it."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _need(t, dtype, name)
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the operands on {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _buf(t, numel, dtype, device, name, alloc=None):
+    """A flat output or workspace of at least `numel` elements: allocated
+    (`alloc` elements, default numel) if None, else checked."""
+    if t is None:
+        return torch.empty(max(numel, alloc or 0, 1), dtype=dtype, device=device)
+    _need(t, dtype, name)
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the operands on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs at least {numel}")
+    return t
+
+
+def _mat(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D, got {t.dim()}-D")
+    return t
 
 
 # ------------------------------------------------------------------ weights
@@ -135,16 +186,15 @@ def w8a8_weight_workspace_bytes(N, K):
 def w8a8_quant_weight_tensorwise(w, qtype=INT8, transposed=False, out=None, out_t=None, scale=None,
                                  workspace=None):
     """w: bf16 [N, K].  Returns (codes [N, K], codes^T [K, N] or None, scale f32 [1])."""
+    cd = _code_dtype(qtype)
     _need(w, torch.bfloat16, "w")
-    w = w.contiguous()
-    N, K = w.shape
     dev = w.device
-    wq = out if out is not None else torch.empty((N, K), dtype=_code_dtype(qtype), device=dev)
-    wq_t = out_t if out_t is not None else (
-        torch.empty((K, N), dtype=_code_dtype(qtype), device=dev) if transposed else None)
-    s = scale if scale is not None else torch.empty(4, dtype=torch.float32, device=dev)
-    ws = workspace if workspace is not None else torch.empty(
-        w8a8_weight_workspace_bytes(N, K), dtype=torch.uint8, device=dev)
+    w = _mat(_arg(w, torch.bfloat16, "w", dev), "w")
+    N, K = w.shape
+    wq = _out(out, (N, K), cd, dev, "out")
+    wq_t = _out(out_t, (K, N), cd, dev, "out_t") if (transposed or out_t is not None) else None
+    s = _buf(scale, 1, torch.float32, dev, "scale", alloc=4)
+    ws = _buf(workspace, w8a8_weight_workspace_bytes(N, K), torch.uint8, dev, "workspace")
     _check(_lib.w8a8_quant_weight_tensorwise(qtype, _ptr(w), N, K, _ptr(wq), _ptr(wq_t), _ptr(s), _ptr(ws),
                                              _stream(dev)))
     return wq, wq_t, s[:1]
@@ -153,6 +203,7 @@ def w8a8_quant_weight_tensorwise(w, qtype=INT8, transposed=False, out=None, out_
 # -------------------------------------------------------------- activations
 def w8a8_quant_act_rowwise(x, qtype=INT8, ldq=None, out=None, scale=None):
     """x: bf16 [M, K] (row stride may exceed K).  Returns (codes [M, ldq], scales f32 [M])."""
+    cd = _code_dtype(qtype)
     _need(x, torch.bfloat16, "x")
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
@@ -165,52 +216,63 @@ def w8a8_quant_act_rowwise(x, qtype=INT8, ldq=None, out=None, scale=None):
     ldx = x.stride(0) if M > 1 else K + (-K) % 8
     ldq = ldq if ldq is not None else K + (-K) % 16
     dev = x.device
-    xq = out if out is not None else torch.empty((M, ldq), dtype=_code_dtype(qtype), device=dev)
-    s = scale if scale is not None else torch.empty(M, dtype=torch.float32, device=dev)
+    xq = _out(out, (M, ldq), cd, dev, "out")
+    s = _buf(scale, M, torch.float32, dev, "scale")
     _check(_lib.w8a8_quant_act_rowwise(qtype, _ptr(x), M, K, ldx, _ptr(xq), ldq, _ptr(s), _stream(dev)))
-    return xq, s
+    return xq, s[:M]
 
 
 def w8a8_quant_act_rowwise_hadamard(x, qtype=INT8, ldq=None, out=None, scale=None):
     """x: bf16 [M, K], K % 16 == 0.  Codes [M, ldq] and scales [M] of the Hadamard-rotated rows."""
+    cd = _code_dtype(qtype)
     _need(x, torch.bfloat16, "x")
-    x = x.contiguous()
+    dev = x.device
+    x = _mat(_arg(x, torch.bfloat16, "x", dev), "x")
     M, K = x.shape
     ldq = ldq if ldq is not None else K
-    dev = x.device
-    xq = out if out is not None else torch.empty((M, ldq), dtype=_code_dtype(qtype), device=dev)
-    s = scale if scale is not None else torch.empty(M, dtype=torch.float32, device=dev)
+    xq = _out(out, (M, ldq), cd, dev, "out")
+    s = _buf(scale, M, torch.float32, dev, "scale")
     _check(_lib.w8a8_quant_act_rowwise_hadamard(qtype, _ptr(x), M, K, K, _ptr(xq), ldq, _ptr(s), _stream(dev)))
-    return xq, s
+    return xq, s[:M]
 
 
 def w8a8_hadamard_rotate(x, out=None):
     """x: bf16 [M, K], K % 16 == 0 -> bf16 [M, K] rotated rows."""
     _need(x, torch.bfloat16, "x")
-    x = x.contiguous()
+    dev = x.device
+    x = _mat(_arg(x, torch.bfloat16, "x", dev), "x")
     M, K = x.shape
-    y = out if out is not None else torch.empty((M, K), dtype=torch.bfloat16, device=x.device)
-    _check(_lib.w8a8_hadamard_rotate(_ptr(x), M, K, K, _ptr(y), K, _stream(x.device)))
+    y = _out(out, (M, K), torch.bfloat16, dev, "out")
+    _check(_lib.w8a8_hadamard_rotate(_ptr(x), M, K, K, _ptr(y), K, _stream(dev)))
     return y
 
 
 # --------------------------------------------------------------- the linear
-def w8a8_linear(xq, x_scale, wq, w_scale, bias=None, out=None):
-    """Dequantized 8-bit linear.  xq [M, K], wq [N, K] codes (same dtype) -> bf16 [M, N]."""
+def _product_args(xq, x_scale, wq, w_scale, w_scale_numel, bias):
     qt = _qtype_of(xq)
     if wq.dtype != xq.dtype:
         raise TypeError("xq and wq must hold the same code type")
+    _need(xq, None, "xq")
+    dev = xq.device
+    xq = _mat(_arg(xq, None, "xq", dev), "xq")
+    wq = _mat(_arg(wq, None, "wq", dev), "wq")
     M, K = xq.shape
     N = wq.shape[0]
     if wq.shape[1] != K:
         raise ValueError("xq and wq must share K")
-    _need(x_scale, torch.float32, "x_scale")
-    _need(w_scale, torch.float32, "w_scale")
+    x_scale = _arg(x_scale, torch.float32, "x_scale", dev, M)
+    w_scale = _arg(w_scale, torch.float32, "w_scale", dev, w_scale_numel(N))
     if bias is not None:
-        _need(bias, torch.bfloat16, "bias")
-    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+        bias = _arg(bias, torch.bfloat16, "bias", dev, N)
+    return qt, dev, xq, x_scale, wq, w_scale, bias, M, N, K
+
+
+def w8a8_linear(xq, x_scale, wq, w_scale, bias=None, out=None):
+    """Dequantized 8-bit linear.  xq [M, K], wq [N, K] codes (same dtype) -> bf16 [M, N]."""
+    qt, dev, xq, x_scale, wq, w_scale, bias, M, N, K = _product_args(xq, x_scale, wq, w_scale, lambda n: 1, bias)
+    y = _out(out, (M, N), torch.bfloat16, dev, "out")
     _check(_lib.w8a8_linear(qt, _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(bias), M, N, K, _ptr(y),
-                            _stream(xq.device)))
+                            _stream(dev)))
     return y
 
 
@@ -219,24 +281,34 @@ def w8a8_linear_backward_dx(dyq, dy_scale, wq_t, w_scale, out=None):
     qt = _qtype_of(dyq)
     if wq_t.dtype != dyq.dtype:
         raise TypeError("dyq and wq_t must hold the same code type")
+    _need(dyq, None, "dyq")
+    dev = dyq.device
+    dyq = _mat(_arg(dyq, None, "dyq", dev), "dyq")
+    wq_t = _mat(_arg(wq_t, None, "wq_t", dev), "wq_t")
     M, N = dyq.shape
     K = wq_t.shape[0]
     if wq_t.shape[1] != N:
         raise ValueError("dyq and wq_t must share N")
-    dx = out if out is not None else torch.empty((M, K), dtype=torch.bfloat16, device=dyq.device)
+    dy_scale = _arg(dy_scale, torch.float32, "dy_scale", dev, M)
+    w_scale = _arg(w_scale, torch.float32, "w_scale", dev, 1)
+    dx = _out(out, (M, K), torch.bfloat16, dev, "out")
     _check(_lib.w8a8_linear_backward_dx(qt, _ptr(dyq), _ptr(dy_scale), _ptr(wq_t), _ptr(w_scale), M, N, K,
-                                        _ptr(dx), _stream(dyq.device)))
+                                        _ptr(dx), _stream(dev)))
     return dx
 
 
 def w8a8_gemm_i32(xq, wq, out=None):
     """Raw int32 accumulators of the int8 product: xq [M, K] @ wq[N, K]^T."""
     _need(xq, torch.int8, "xq")
-    _need(wq, torch.int8, "wq")
+    dev = xq.device
+    xq = _mat(_arg(xq, torch.int8, "xq", dev), "xq")
+    wq = _mat(_arg(wq, torch.int8, "wq", dev), "wq")
     M, K = xq.shape
     N = wq.shape[0]
-    acc = out if out is not None else torch.empty((M, N), dtype=torch.int32, device=xq.device)
-    _check(_lib.w8a8_gemm_i32(_ptr(xq), _ptr(wq), M, N, K, _ptr(acc), _stream(xq.device)))
+    if wq.shape[1] != K:
+        raise ValueError("xq and wq must share K")
+    acc = _out(out, (M, N), torch.int32, dev, "out")
+    _check(_lib.w8a8_gemm_i32(_ptr(xq), _ptr(wq), M, N, K, _ptr(acc), _stream(dev)))
     return acc
 
 
@@ -250,22 +322,28 @@ def svdq_linear(x, rq, r_scale, l1, l2, bias=None, out=None, xq_out=None, x_scal
     Returns (y bf16 [M, N], xq [M, K], x_scale [M])."""
     qt = _qtype_of(rq)
     _need(x, torch.bfloat16, "x")
-    _need(l1, torch.bfloat16, "l1")
-    _need(l2, torch.bfloat16, "l2")
-    x = x.contiguous()
+    dev = x.device
+    x = _mat(_arg(x, torch.bfloat16, "x", dev), "x")
+    rq = _mat(_arg(rq, None, "rq", dev), "rq")
+    l1 = _mat(_arg(l1, torch.bfloat16, "l1", dev), "l1")
+    l2 = _mat(_arg(l2, torch.bfloat16, "l2", dev), "l2")
     M, K = x.shape
     N = rq.shape[0]
     r = l1.shape[0]
-    dev = x.device
-    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    xq = xq_out if xq_out is not None else torch.empty((M, K), dtype=rq.dtype, device=dev)
-    sx = x_scale_out if x_scale_out is not None else torch.empty(M, dtype=torch.float32, device=dev)
-    ws = workspace if workspace is not None else torch.empty(max(svdq_workspace_bytes(M, r), 16),
-                                                             dtype=torch.uint8, device=dev)
-    _check(_lib.svdq_linear(qt, _ptr(x), M, K, _ptr(rq), _ptr(r_scale), _ptr(l1.contiguous()),
-                            _ptr(l2.contiguous()), r, _ptr(bias), N, _ptr(y), _ptr(xq), _ptr(sx), _ptr(ws),
-                            _stream(dev)))
-    return y, xq, sx
+    if rq.shape[1] != K or l1.shape[1] != K:
+        raise ValueError("x, rq and l1 must share K")
+    if tuple(l2.shape) != (N, r):
+        raise ValueError(f"l2 must be [N, r] = [{N}, {r}], got {tuple(l2.shape)}")
+    r_scale = _arg(r_scale, torch.float32, "r_scale", dev, 1)
+    if bias is not None:
+        bias = _arg(bias, torch.bfloat16, "bias", dev, N)
+    y = _out(out, (M, N), torch.bfloat16, dev, "out")
+    xq = _out(xq_out, (M, K), rq.dtype, dev, "xq_out")
+    sx = _buf(x_scale_out, M, torch.float32, dev, "x_scale_out")
+    ws = _buf(workspace, svdq_workspace_bytes(M, r), torch.uint8, dev, "workspace", alloc=16)
+    _check(_lib.svdq_linear(qt, _ptr(x), M, K, _ptr(rq), _ptr(r_scale), _ptr(l1), _ptr(l2), r, _ptr(bias), N,
+                            _ptr(y), _ptr(xq), _ptr(sx), _ptr(ws), _stream(dev)))
+    return y, xq, sx[:M]
 
 
 def svdq_prepare_subspace(r):
@@ -280,19 +358,18 @@ def svdq_prepare(w, r, omega, iters=2, l1=None, l2=None, residual=None, sigma=No
     """w bf16 [N, K]; omega bf16 [svdq_prepare_subspace(r), K] (Gaussian).
     Returns (l1 bf16 [r, K], l2 bf16 [N, r], residual bf16 [N, K], sigma f32 [r])."""
     _need(w, torch.bfloat16, "w")
-    _need(omega, torch.bfloat16, "omega")
-    w = w.contiguous()
+    dev = w.device
+    w = _mat(_arg(w, torch.bfloat16, "w", dev), "w")
+    omega = _arg(omega, torch.bfloat16, "omega", dev)
     N, K = w.shape
     if tuple(omega.shape) != (svdq_prepare_subspace(r), K):
         raise ValueError("omega must be [svdq_prepare_subspace(r), K]")
-    dev = w.device
-    l1 = l1 if l1 is not None else torch.empty((r, K), dtype=torch.bfloat16, device=dev)
-    l2 = l2 if l2 is not None else torch.empty((N, r), dtype=torch.bfloat16, device=dev)
-    res = residual if residual is not None else torch.empty((N, K), dtype=torch.bfloat16, device=dev)
-    sg = sigma if sigma is not None else torch.empty(max(r, 4), dtype=torch.float32, device=dev)
-    ws = workspace if workspace is not None else torch.empty(max(svdq_prepare_workspace_bytes(N, K, r), 16),
-                                                             dtype=torch.uint8, device=dev)
-    _check(_lib.svdq_prepare(_ptr(w), N, K, r, _ptr(omega.contiguous()), iters, _ptr(l1), _ptr(l2), _ptr(res),
+    l1 = _out(l1, (r, K), torch.bfloat16, dev, "l1")
+    l2 = _out(l2, (N, r), torch.bfloat16, dev, "l2")
+    res = _out(residual, (N, K), torch.bfloat16, dev, "residual")
+    sg = _buf(sigma, r, torch.float32, dev, "sigma", alloc=4)
+    ws = _buf(workspace, svdq_prepare_workspace_bytes(N, K, r), torch.uint8, dev, "workspace", alloc=16)
+    _check(_lib.svdq_prepare(_ptr(w), N, K, r, _ptr(omega), iters, _ptr(l1), _ptr(l2), _ptr(res),
                              _ptr(sg), _ptr(ws), _stream(dev)))
     return l1, l2, res, sg[:r]
 
@@ -305,48 +382,43 @@ def q8_0_nbytes(n):
 def q8_0_quantize(x, out=None):
     """x f32 (any shape, contiguous) -> uint8 [q8_0_nbytes(x.numel())] GGUF Q8_0 blocks."""
     _need(x, torch.float32, "x")
-    x = x.contiguous()
+    dev = x.device
+    x = _arg(x, torch.float32, "x", dev)
     n = x.numel()
-    blocks = out if out is not None else torch.empty(max(q8_0_nbytes(n), 16), dtype=torch.uint8, device=x.device)
-    _check(_lib.q8_0_quantize(_ptr(x), n, _ptr(blocks), _stream(x.device)))
+    blocks = _buf(out, q8_0_nbytes(n), torch.uint8, dev, "out", alloc=16)
+    _check(_lib.q8_0_quantize(_ptr(x), n, _ptr(blocks), _stream(dev)))
     return blocks[:q8_0_nbytes(n)]
 
 
 def q8_0_dequantize(blocks, n, out=None):
     """blocks uint8 (>= q8_0_nbytes(n) bytes) -> f32 [n]."""
     _need(blocks, torch.uint8, "blocks")
-    y = out if out is not None else torch.empty(max(n, 4), dtype=torch.float32, device=blocks.device)
-    _check(_lib.q8_0_dequantize(_ptr(blocks), n, _ptr(y), _stream(blocks.device)))
+    dev = blocks.device
+    blocks = _arg(blocks, torch.uint8, "blocks", dev, q8_0_nbytes(n))
+    y = _buf(out, n, torch.float32, dev, "out", alloc=4)
+    _check(_lib.q8_0_dequantize(_ptr(blocks), n, _ptr(y), _stream(dev)))
     return y[:n]
 
 
 # ------------------------------------------------------------------- GGUF A8
 def gguf_a8_requant_q8_0(blocks, N, K, qtype=INT8, out=None, scale=None):
     """Q8_0 weight [N, K] (uint8 blocks, row n = K / 32 blocks) -> (codes [N, K], scales f32 [N])."""
+    cd = _code_dtype(qtype)
     _need(blocks, torch.uint8, "blocks")
     dev = blocks.device
-    wq = out if out is not None else torch.empty((N, K), dtype=_code_dtype(qtype), device=dev)
-    s = scale if scale is not None else torch.empty(max(N, 4), dtype=torch.float32, device=dev)
+    blocks = _arg(blocks, torch.uint8, "blocks", dev, q8_0_nbytes(N * K) if K % 32 == 0 else 0)
+    wq = _out(out, (N, K), cd, dev, "out")
+    s = _buf(scale, N, torch.float32, dev, "scale", alloc=4)
     _check(_lib.gguf_a8_requant_q8_0(qtype, _ptr(blocks), N, K, _ptr(wq), _ptr(s), _stream(dev)))
     return wq, s[:N]
 
 
 def gguf_a8_linear(xq, x_scale, wq, w_scale, bias=None, out=None):
     """8-bit linear with per-output-channel weight scales w_scale f32 [N] -> bf16 [M, N]."""
-    qt = _qtype_of(xq)
-    if wq.dtype != xq.dtype:
-        raise TypeError("xq and wq must hold the same code type")
-    M, K = xq.shape
-    N = wq.shape[0]
-    if wq.shape[1] != K:
-        raise ValueError("xq and wq must share K")
-    _need(x_scale, torch.float32, "x_scale")
-    _need(w_scale, torch.float32, "w_scale")
-    if bias is not None:
-        _need(bias, torch.bfloat16, "bias")
-    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=xq.device)
+    qt, dev, xq, x_scale, wq, w_scale, bias, M, N, K = _product_args(xq, x_scale, wq, w_scale, lambda n: n, bias)
+    y = _out(out, (M, N), torch.bfloat16, dev, "out")
     _check(_lib.gguf_a8_linear(qt, _ptr(xq), _ptr(x_scale), _ptr(wq), _ptr(w_scale), _ptr(bias), M, N, K, _ptr(y),
-                               _stream(xq.device)))
+                               _stream(dev)))
     return y
 
 
@@ -361,7 +433,6 @@ def probe_mfma_i8(a, b, pairs, sink=None):
         if t.numel() * t.element_size() < 65536 or not t.is_contiguous():
             raise ValueError("probe operands: contiguous, at least 65536 bytes")
     n = _lib.w8a8_probe_sink_count()
-    if sink is None:
-        sink = torch.empty(n, dtype=torch.int32, device=a.device)
+    sink = _buf(sink, n, torch.int32, a.device, "sink")
     _check(_lib.w8a8_probe_mfma_i8(_ptr(a), _ptr(b), int(pairs), _ptr(sink), _stream(a.device)))
     return sink
