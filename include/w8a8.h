@@ -94,7 +94,7 @@ size_t w8a8_weight_workspace_bytes(int64_t N, int64_t K);
  *          (partial maxima; no clearing needed).
  * Two kernels: per-block partial maxima, then a kernel that re-reduces them
  * (deterministic, no atomics) and writes the codes.
- * Shape rules: N, K >= 0; K % 8 == 0.
+ * Shape rules: N, K >= 0; K % 8 == 0; N, K <= 2^31 and N * K <= 2^40.
  */
 w8a8_status w8a8_quant_weight_tensorwise(w8a8_qtype qtype, const uint16_t *w, int64_t N, int64_t K,
                                          void *wq, void *wq_t, float *w_scale, void *workspace,
@@ -112,7 +112,8 @@ w8a8_status w8a8_quant_weight_tensorwise(w8a8_qtype qtype, const uint16_t *w, in
  *   xq     codes [M, ldq]; columns K .. ldq-1 are written as zero, so a
  *          caller can pad K up to the 16-multiple the GEMM needs.
  *   x_scale f32 [M].
- * Shape rules: M, K >= 0; ldx >= K, ldx % 8 == 0; ldq >= K, ldq % 16 == 0.
+ * Shape rules: M, K >= 0; K <= 2^30; ldx >= K, ldx % 8 == 0; ldq >= K,
+ * ldq % 16 == 0.
  */
 w8a8_status w8a8_quant_act_rowwise(w8a8_qtype qtype, const uint16_t *x, int64_t M, int64_t K,
                                    int64_t ldx, void *xq, int64_t ldq, float *x_scale,
@@ -129,7 +130,8 @@ w8a8_status w8a8_quant_act_rowwise(w8a8_qtype qtype, const uint16_t *x, int64_t 
  *   xq [M, K] codes, x_scale f32 [M]; wq [N, K] codes, w_scale one f32;
  *   bias bf16 [N] or NULL; y bf16 [M, N].
  * Shape rules: M, N >= 0; K >= 16, K % 16 == 0 (pad K with zero codes: a zero
- * code adds exactly 0).  Any M and N, including ragged tile tails.  The int32
+ * code adds exactly 0); M, N <= 2^30, K <= 2^22.  Any M and N, including
+ * ragged tile tails.  The int32
  * sum is exact while |acc| < 2^31: always for codes the quantizers produce
  * (|q| <= 127) when K <= 133143, since 127^2 K < 2^31.
  */
@@ -144,7 +146,7 @@ w8a8_status w8a8_linear(w8a8_qtype qtype, const void *xq, const float *x_scale, 
  * w8a8_quant_weight_tensorwise (wq_t [K, N], w_scale):
  *   dx[m, k] = bf16(sum_n dyq[m, n] * wq_t[k, n] * dy_scale[m] * w_scale[0]).
  * The same product kernel as w8a8_linear with the roles (K <- N, N <- K).
- * Shape rules: M, K >= 0; N >= 16, N % 16 == 0.
+ * Shape rules: M, K >= 0; N >= 16, N % 16 == 0; M, K <= 2^30, N <= 2^22.
  */
 w8a8_status w8a8_linear_backward_dx(w8a8_qtype qtype, const void *dyq, const float *dy_scale,
                                     const void *wq_t, const float *w_scale, int64_t M, int64_t N,
@@ -246,9 +248,11 @@ w8a8_status q8_0_dequantize(const void *blocks, int64_t n, float *y, hipStream_t
  * then times c = f32(1 / sqrt(b)); bit-reproducible.
  *
  * w8a8_quant_act_rowwise_hadamard: as w8a8_quant_act_rowwise, on the rotated
- * rows (the shared absmax rule on the f32 rotated values).  K % 16 == 0.
+ * rows (the shared absmax rule on the f32 rotated values).  K % 16 == 0,
+ * 0 < K <= 2^30.
  * w8a8_hadamard_rotate: out bf16 [M, ldo] = the rotated rows of x rounded to
- * bf16 (for the weight, which is then quantized as any weight).  K % 16 == 0.
+ * bf16 (for the weight, which is then quantized as any weight).  K % 16 == 0,
+ * K <= 2^30, ldx >= K, ldo >= K.
  */
 w8a8_status w8a8_quant_act_rowwise_hadamard(w8a8_qtype qtype, const uint16_t *x, int64_t M, int64_t K, int64_t ldx,
                                             void *xq, int64_t ldq, float *x_scale, hipStream_t stream);

@@ -57,6 +57,8 @@ def test_act_quant_rejects():
     assert f(0, MIS, 4, 64, 64, A, 64, A, NULL) == ALIGN
     assert f(1, A, 4, 64, 64, A, 64, MIS, NULL) == ALIGN
     assert f(0, NULL, 0, 64, 64, NULL, 64, NULL, NULL) == OK       # M = 0: no-op
+    big = (1 << 30) + 16
+    assert f(0, A, 4, big, big, A, big, A, NULL) == SHAPE          # K > 2^30
 
 
 def test_linear_rejects():
@@ -76,6 +78,12 @@ def test_linear_rejects():
     assert g(A, A, 8, 8, 32, MIS, NULL) == ALIGN
     b = lib.w8a8_linear_backward_dx
     assert b(1, A, A, A, A, 8, 24, 32, A, NULL) == SHAPE           # reduction N % 16
+    # size limits: K <= 2^22 (the reduction), M, N <= 2^30
+    assert f(0, A, A, A, A, NULL, 64, 64, (1 << 22) + 16, A, NULL) == SHAPE
+    assert f(0, A, A, A, A, NULL, (1 << 30) + 1, 64, 64, A, NULL) == SHAPE
+    assert f(0, A, A, A, A, NULL, 64, (1 << 30) + 1, 64, A, NULL) == SHAPE
+    assert g(A, A, 8, 8, (1 << 22) + 16, A, NULL) == SHAPE
+    assert b(0, A, A, A, A, 8, (1 << 22) + 16, 32, A, NULL) == SHAPE
 
 
 def test_weight_quant_rejects():
@@ -85,6 +93,8 @@ def test_weight_quant_rejects():
     assert f(0, A, 64, 64, A, NULL, A, NULL, NULL) == INVALID      # no workspace
     assert f(0, A, 64, 64, MIS, NULL, A, A, NULL) == ALIGN
     assert f(3, A, 64, 64, A, NULL, A, A, NULL) == INVALID
+    assert f(0, A, 1 << 21, 1 << 20, A, NULL, A, A, NULL) == SHAPE  # N * K = 2^41 > 2^40
+    assert f(0, A, 8, (1 << 31) + 8, A, NULL, A, A, NULL) == SHAPE  # K > 2^31
 
 
 def test_svdq_rejects():
@@ -167,3 +177,6 @@ def test_hadamard_rejects():
     assert g(A, -1, 64, 64, A, 64, NULL) == INVALID
     assert g(A, 4, 64, 64, MIS, 64, NULL) == ALIGN
     assert g(NULL, 0, 64, 64, NULL, 64, NULL) == OK
+    big = (1 << 30) + 16
+    assert g(A, 4, big, big, A, big, NULL) == SHAPE                  # K > 2^30
+    assert f(0, A, 4, big, big, A, big, A, NULL) == SHAPE

@@ -104,7 +104,9 @@ __global__ __launch_bounds__(kThreads) void weight_quant_kernel(const uint16_t *
 __global__ __launch_bounds__(kThreads) void transpose_codes_kernel(const uint8_t *__restrict__ wq, int64_t N,
                                                                    int64_t K, uint8_t *__restrict__ wq_t) {
     __shared__ uint8_t tile[64][64 + 4];
-    const int64_t n0 = (int64_t)blockIdx.y * 64, k0 = (int64_t)blockIdx.x * 64;
+    // one-dimensional grid over the 64x64 tiles, k fastest
+    const int64_t kb = (K + 63) / 64;
+    const int64_t n0 = ((int64_t)blockIdx.x / kb) * 64, k0 = ((int64_t)blockIdx.x % kb) * 64;
     // load: 64 rows (n) x 64 bytes (k); each thread moves 16 bytes
     {
         const int rn = threadIdx.x >> 2, ck = (threadIdx.x & 3) * 16;
@@ -156,6 +158,7 @@ extern "C" w8a8_status w8a8_quant_weight_tensorwise(w8a8_qtype qtype, const uint
     if (!w_scale || !workspace) return W8A8_ERR_INVALID_ARG;
     if (N * K > 0 && (!w || !wq)) return W8A8_ERR_INVALID_ARG;
     if (K % 8 != 0 || (wq_t && N % 16 != 0)) return W8A8_ERR_SHAPE;
+    if (N > ((int64_t)1 << 31) || K > ((int64_t)1 << 31) || N * K > ((int64_t)1 << 40)) return W8A8_ERR_SHAPE;
     if (!aligned16(w) || !aligned16(wq) || !aligned16(wq_t) || !aligned16(w_scale) || !aligned16(workspace))
         return W8A8_ERR_ALIGN;
     const int64_t nchunks = N * K / 8;
@@ -170,8 +173,8 @@ extern "C" w8a8_status w8a8_quant_weight_tensorwise(w8a8_qtype qtype, const uint
         weight_quant_kernel<W8A8_FP8_E4M3><<<grid, kThreads, 0, stream>>>(w, nchunks, partial, grid,
                                                                           static_cast<uint8_t *>(wq), w_scale);
     if (wq_t && nchunks > 0) {
-        dim3 g((unsigned)((K + 63) / 64), (unsigned)((N + 63) / 64));
-        transpose_codes_kernel<<<g, kThreads, 0, stream>>>(static_cast<const uint8_t *>(wq), N, K,
+        const int64_t tiles = ((K + 63) / 64) * ((N + 63) / 64);  // <= 2^28 by the limits above
+        transpose_codes_kernel<<<(unsigned)tiles, kThreads, 0, stream>>>(static_cast<const uint8_t *>(wq), N, K,
                                                            static_cast<uint8_t *>(wq_t));
     }
     return launch_status();
