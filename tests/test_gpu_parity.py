@@ -178,6 +178,29 @@ def test_gemm_i32_longest_exact_k():
     assert_equal(acc.cpu().numpy(), ref, "int32 accumulators at the longest exact K")
 
 
+def test_gemm_i32_max_k():
+    """K at its limit (2^22, 65,536 stages through one tile) with ragged M, N;
+    random codes keep |acc| far below 2^31, so the sum is exact."""
+    _say("gemm_i32 M3 N5 K=2^22")
+    rng = np.random.default_rng(17)
+    M, N, K = 3, 5, 1 << 22
+    a = rng.integers(-128, 128, (M, K), dtype=np.int8)
+    b = rng.integers(-128, 128, (N, K), dtype=np.int8)
+    acc = W8.w8a8_gemm_i32(codes_dev(a, False), codes_dev(b, False))
+    torch.cuda.synchronize()
+    assert_equal(acc.cpu().numpy(), oracle.gemm_i32(a, b), "accumulators at K = 2^22")
+
+
+def test_act_quant_longest_rows():
+    """Rows of 2^22 + 16 values (the two-pass kernel), both code types."""
+    K = (1 << 22) + 16
+    rng = np.random.default_rng(19)
+    x = workloads.f32_to_bf16_bits((rng.standard_normal((2, K)) * np.array([[1.0], [300.0]])).astype(np.float32))
+    for qt in (INT8, FP8):
+        _say(f"act_quant K={K} qt={qt}")
+        _act_quant_check(x, qt, what=f"K={K}")
+
+
 def test_gemm_i32_full_size_sampled():
     _say("gemm_i32 M4096 N12288 K3072 sampled rows")
     rng = np.random.default_rng(11)
