@@ -62,7 +62,7 @@ typedef enum {
     W8A8_ERR_INVALID_ARG = 1, /* null required pointer, negative size, bad enum, r outside [1, 64] */
     W8A8_ERR_SHAPE = 2,       /* a size or stride that the layout rules below forbid */
     W8A8_ERR_ALIGN = 3,       /* a pointer that is not 16-byte aligned */
-    W8A8_ERR_UNSUPPORTED = 4, /* a combination this build does not implement */
+    W8A8_ERR_UNSUPPORTED = 4, /* a combination the library does not implement */
     W8A8_ERR_HIP = 5          /* the HIP runtime reported a launch error */
 } w8a8_status;
 
