@@ -92,10 +92,11 @@ def _traffic_from_profile(kernel_hash):
     if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(path):
-        if "=" in line and not line.startswith("#"):
-            k, v = line.split("=", 1)
-            vals[k.strip()] = v.strip()
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                vals[k.strip()] = v.strip()
     if vals.get("kernel_source_hash") != kernel_hash:
         return None
     try:

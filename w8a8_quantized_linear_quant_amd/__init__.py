@@ -85,7 +85,8 @@ _lib = _load_library()
 
 def exported_names_in_header(path=HEADER):
     """Function names the C header declares (used to check the exports)."""
-    text = open(path).read()
+    with open(path) as f:
+        text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\(", text)) -
                   {"if", "defined", "sizeof", "extern"})
