@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 PEAK_INT8_TOPS = 5000.0     # MI355X dense int8 MFMA, 5.0 POPS
 PEAK_FP8_TFLOPS = 5000.0    # dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0       # HBM3E 8 TB/s
+PEAK_VALU_LANE_TOPS = 39.32  # non-packed f32 VALU lane operations: 256 CU x 4 SIMD x 16 lanes x 2.4 GHz
 M, K, N = 4096, 3072, 12288
 ROTATE = 4       # buffer sets of the step (4 x 150 MB, past the 256 MB Infinity Cache)
 AQ_ROTATE = 16   # buffer sets of the act-quant timing (16 x 38 MB: every launch reads cold HBM)
@@ -397,6 +398,13 @@ def other_rows(w8, torch, workloads, args):
                                                                 scale=hs[i % AQ_ROTATE][2]))
     res["act_quant_hadamard_int8_X4096x3072"] = {"us": round(ms * 1e3, 1),
                                                  "GB/s": round((3.0 * M * K + 4 * M) / ms / 1e6, 1)}
+    # its VALU side: M K (log2 b + 2) lane operations (the transform's sums and
+    # differences, one absmax and one division per element) against plain f32
+    # issue, 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3 T lane-ops/s
+    lane_ops = float(M * K * (10 + 2))
+    res["act_quant_hadamard_int8_X4096x3072"]["alu"] = {
+        "lane_ops_per_launch": lane_ops, "achieved_T_per_s": round(lane_ops / ms / 1e9, 2),
+        "peak_T_per_s": PEAK_VALU_LANE_TOPS, "frac": round(lane_ops / ms / 1e9 / PEAK_VALU_LANE_TOPS, 4)}
     del xh0, hs
     # SVDQuant weight preparation of the SVDQuant workload's weight, r = 32, 2 power iterations
     d = workloads.svdq()
