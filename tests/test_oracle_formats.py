@@ -111,3 +111,44 @@ def test_e4m3_midpoints_tie_to_even():
 @pytest.mark.parametrize("v,code", [(448.0, 0x7E), (460.0, 0x7E), (-448.0, 0xFE), (-0.0, 0x80), (0.0, 0x00)])
 def test_e4m3_edges(v, code):
     assert int(oracle.f32_to_e4m3(np.float32([v]))[0]) == code
+
+
+def test_absmax_scale_rule_and_floor():
+    # s = 1e-10f when absmax < 1e-10f, else f32(absmax / qmax) -- one rounding
+    floor = np.float32(1e-10)
+    assert oracle.absmax_scale(0.0, 127.0) == floor
+    assert oracle.absmax_scale(np.nextafter(floor, np.float32(0)), 127.0) == floor
+    assert oracle.absmax_scale(floor, 127.0) == np.float32(np.float32(1e-10) / np.float32(127.0))  # not floored
+    assert oracle.absmax_scale(127.0, 127.0) == np.float32(1.0)
+    assert oracle.absmax_scale(448.0, 448.0) == np.float32(1.0)
+    rng = np.random.default_rng(5)
+    for a in (rng.random(2000) * 10.0 ** rng.integers(-9, 6, 2000)).astype(np.float32):
+        for q in (127.0, 448.0):
+            want = np.float32(a) / np.float32(q) if a >= floor else floor
+            assert oracle.absmax_scale(a, q) == want, (a, q)
+
+
+def test_f64_to_f16_rounds_once_from_double():
+    # numpy's float64 -> float16 cast rounds once, directly
+    rng = np.random.default_rng(6)
+    v = rng.standard_normal(200_000) * 10.0 ** rng.integers(-8, 5, 200_000)
+    with np.errstate(over="ignore"):
+        ref = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(oracle.f64_to_f16(v), ref)
+    # a tie of f16 that is not a tie in double: 1 + 2^-11 is the midpoint of
+    # 1 and 1 + 2^-10; a hair above it must round up, which rounding through
+    # f32 first (to the exact midpoint, then to even) would miss
+    h = oracle.f64_to_f16(np.array([1 + 2.0**-11, 1 + 2.0**-11 + 2.0**-40, 1 + 2.0**-11 - 2.0**-40]))
+    assert h.tolist() == [0x3C00, 0x3C01, 0x3C00]
+
+
+def test_f64_to_e4m3_rounds_once_from_double():
+    # 1.0625 is the midpoint of e4m3 1.0 (0x38) and 1.125 (0x39): ties to the
+    # even code 0x38; just above it 0x39 (f32 would first round it to 1.0625)
+    e = oracle.f64_to_e4m3(np.array([1.0625, 1.0625 + 2.0**-40, 1.0625 - 2.0**-40, -1.0625 - 2.0**-40]))
+    assert e.tolist() == [0x38, 0x39, 0x38, 0xB9]
+    # wherever a double is exactly an f32, the direct and the f32 paths agree
+    rng = np.random.default_rng(7)
+    f = (rng.standard_normal(100_000) * 10.0 ** rng.integers(-4, 3, 100_000)).astype(np.float32)
+    f = np.clip(f, -448, 448)
+    assert np.array_equal(oracle.f64_to_e4m3(f.astype(np.float64)), oracle.f32_to_e4m3(f))

@@ -98,3 +98,20 @@ def test_residual_identity():
 def test_zero_matrix(r):
     sig, l1b, l2b, rb = svd_prep.svdq_prepare(np.zeros((64, 32), np.uint16), min(r, 32))
     assert np.all(sig == 0) and not l1b.any() and not l2b.any() and not rb.any()
+
+
+def test_low_rank_and_residual_definitions():
+    # hand-computed: l2 . l1 of these bf16-exact factors, and W = l2 . l1 + E
+    # with every entry of W exact in bf16, so the residual must be E exactly
+    # (a swapped operand, a sign or a transposition changes it)
+    l2 = oracle.f64_to_bf16(np.array([[1.0, 0.5], [-2.0, 0.25], [0.0, 4.0]]))
+    l1 = oracle.f64_to_bf16(np.array([[0.5, -1.0, 2.0, 0.0], [8.0, 0.125, -0.5, 1.0]]))
+    p = np.array([[4.5, -0.9375, 1.75, 0.5],
+                  [1.0, 2.03125, -4.125, 0.25],
+                  [32.0, 0.5, -2.0, 4.0]])
+    assert np.array_equal(svd_prep.low_rank(l2, l1), p)
+    e = np.array([[0.5, 0.0, 0.0, -0.5], [0.0, 0.25, 0.0, 0.0], [1.0, 0.0, 0.0, 0.5]])
+    w = oracle.f64_to_bf16(p + e)
+    assert np.array_equal(oracle.bf16_to_f64(w), p + e)          # W is exact in bf16
+    assert np.array_equal(oracle.bf16_to_f64(svd_prep.residual(w, l2, l1)), e)
+    assert not svd_prep.residual(oracle.f64_to_bf16(p), l2, l1).any()
