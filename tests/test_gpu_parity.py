@@ -719,6 +719,98 @@ def test_determinism_and_graph_capture():
     del d
 
 
+def _graph_case(name):
+    """(step, outputs) of one entry point on small inputs; step() writes into
+    the preallocated outputs only."""
+    rng = np.random.default_rng(23)
+    M, N, K = 96, 160, 256
+    x = bf16_dev(workloads.activations_bf16(rng, M, K, outliers=2))
+    w = bf16_dev(workloads.normal_bf16(rng, (N, K), 0.02))
+    bias = bf16_dev(workloads.normal_bf16(rng, (N,), 0.02))
+    dev = x.device
+    if name == "weight_quant":
+        wq = torch.empty((N, K), dtype=torch.int8, device=dev)
+        wqt = torch.empty((K, N), dtype=torch.int8, device=dev)
+        sw = torch.empty(4, dtype=torch.float32, device=dev)
+        ws = torch.empty(W8.w8a8_weight_workspace_bytes(N, K), dtype=torch.uint8, device=dev)
+        return (lambda: W8.w8a8_quant_weight_tensorwise(w, transposed=True, out=wq, out_t=wqt, scale=sw,
+                                                         workspace=ws)), [wq, wqt, sw[:1]]
+    if name == "backward_dx":
+        wq, wqt, sw = W8.w8a8_quant_weight_tensorwise(w, qtype=FP8, transposed=True)
+        dy = bf16_dev(workloads.normal_bf16(rng, (M, N), 1e-3))
+        dyq, sdy = W8.w8a8_quant_act_rowwise(dy, qtype=FP8)
+        dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        return (lambda: W8.w8a8_linear_backward_dx(dyq, sdy, wqt, sw, out=dx)), [dx]
+    if name.startswith("svdq"):
+        r = 32 if name == "svdq_r32" else 8
+        l1 = bf16_dev(workloads.normal_bf16(rng, (r, K), 0.1))
+        l2 = bf16_dev(workloads.normal_bf16(rng, (N, r), 0.1))
+        rq, _, sr = W8.w8a8_quant_weight_tensorwise(w)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+        sx = torch.empty(M, dtype=torch.float32, device=dev)
+        ws = torch.empty(W8.svdq_workspace_bytes(M, r), dtype=torch.uint8, device=dev)
+        return (lambda: W8.svdq_linear(x, rq, sr, l1, l2, bias, out=y, xq_out=xq, x_scale_out=sx,
+                                       workspace=ws)), [y, xq, sx]
+    if name == "q8_0":
+        v = torch.from_numpy((rng.standard_normal(1000) * 3).astype(np.float32)).to(dev)
+        blocks = torch.empty(W8.q8_0_nbytes(1000), dtype=torch.uint8, device=dev)
+        back = torch.empty(1000, dtype=torch.float32, device=dev)
+
+        def q8():
+            W8.q8_0_quantize(v, out=blocks)
+            W8.q8_0_dequantize(blocks, 1000, out=back)
+        return q8, [blocks, back]
+    if name == "gguf_a8":
+        blob = torch.from_numpy(workloads.q8_0_weight_blocks(rng, N, K)).to(dev)
+        wq = torch.empty((N, K), dtype=torch.int8, device=dev)
+        sw = torch.empty(N, dtype=torch.float32, device=dev)
+        xq, sx = W8.w8a8_quant_act_rowwise(x)
+        y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+        def gg():
+            W8.gguf_a8_requant_q8_0(blob, N, K, out=wq, scale=sw)
+            W8.gguf_a8_linear(xq, sx, wq, sw, bias, out=y)
+        return gg, [wq, sw, y]
+    if name == "hadamard":
+        xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+        sx = torch.empty(M, dtype=torch.float32, device=dev)
+        return (lambda: W8.w8a8_quant_act_rowwise_hadamard(x, out=xq, scale=sx)), [xq, sx]
+    raise ValueError(name)
+
+
+@pytest.mark.parametrize("name", ["weight_quant", "backward_dx", "svdq_r32", "svdq_r8", "q8_0", "gguf_a8",
+                                  "hadamard"])
+def test_graph_capture_of_every_entry_point(name):
+    """Each entry point captured in a HIP graph and replayed three times, with
+    the outputs cleared and unrelated eager work between replays: every replay
+    equals the eager result bit for bit."""
+    _say(f"graph capture: {name}")
+    step, outs = _graph_case(name)
+    step()
+    torch.cuda.synchronize()
+    ref = [bytes_host(o).copy() for o in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for i in range(3):
+        for o in outs:
+            o.view(torch.uint8).zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for o, r in zip(outs, ref):
+            assert_equal(bytes_host(o), r, f"{name} replay {i}")
+        _ = torch.randn(1 << 16, device="cuda").sum()      # unrelated eager work between replays
+        torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------ diagnostics
 def test_probe_mfma_runs():
     _say("probe mfma i8")
