@@ -33,6 +33,8 @@
 #include <type_traits>
 #include <utility>
 
+#include <atomic>
+
 #include "internal.hpp"
 
 namespace w8a8 {
@@ -673,17 +675,18 @@ void launch(const GemmArgs &a, hipStream_t stream) {
 
 }  // namespace
 
-// Compute units of the current device (queried once per device).
+// Compute units of the current device (queried once per device; threads
+// that race on the first query store the same value, atomically).
 int device_cu_count() {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64] = {};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 w8a8_status gemm_check(const void *xq, const void *wq, int64_t M, int64_t N, int64_t K, const void *out) {
