@@ -85,19 +85,30 @@ __global__ __launch_bounds__(kThreads) void gguf_a8_requant_row_kernel(const uin
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[i] = (float)(int8_t)(w >> (8 * i)) * d;  // exact in f32
         };
+        // |q d| of this lane's 4 codes of block b, maximized: every product is
+        // exact in f32 (8-bit q, 11-bit d), so the largest is max|q| * |d|.
+        auto block_absmax = [&](int b) {
+            const uint8_t *bp = st + off + b * 34;
+            const uint32_t dbits = *reinterpret_cast<const uint16_t *>(bp);
+            const uint32_t lo = *reinterpret_cast<const uint16_t *>(bp + 2 + 4 * part);
+            const uint32_t hi = *reinterpret_cast<const uint16_t *>(bp + 4 + 4 * part);
+            const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)dbits);
+            const uint32_t w = lo | (hi << 16);
+            float m = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf((float)(int8_t)(w >> (8 * i))));
+            return m * fabsf(d);
+        };
         // Row absmax (non-negative floats order like their bit patterns), 32
         // blocks (4 steps of 8) per iteration with their LDS reads issued
         // together; block indices past the row repeat its last block.
         uint32_t amax_bits = 0;
         for (int b0 = 0; b0 < nb; b0 += 32) {
-            float v[4][4];
+            float a[4];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) block_vals(min(b0 + 8 * q + blk_in_step, nb - 1), v[q]);
+            for (int q = 0; q < 4; ++q) a[q] = block_absmax(min(b0 + 8 * q + blk_in_step, nb - 1));
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float a = fmaxf(fmaxf(fabsf(v[q][0]), fabsf(v[q][1])), fmaxf(fabsf(v[q][2]), fabsf(v[q][3])));
-                amax_bits = max(amax_bits, __float_as_uint(a));
-            }
+            for (int q = 0; q < 4; ++q) amax_bits = max(amax_bits, __float_as_uint(a[q]));
         }
         const float s = absmax_scale(__uint_as_float(wave_max_u32(amax_bits)), qmax);
         const float r = 1.0f / s;
