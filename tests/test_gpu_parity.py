@@ -363,7 +363,10 @@ def test_int8_step_backward_sampled():
 
 # ------------------------------------------------------------ SVDQuant
 @pytest.mark.parametrize("qt", [INT8, FP8])
-@pytest.mark.parametrize("M,K,N,r", [(64, 256, 256, 32), (37, 96, 130, 5), (130, 512, 520, 16), (16, 64, 48, 64)])
+# K > 4096 takes the two-kernel act-quant + down path; r = 24 rounds up to 32
+# but reads the factors from global memory in the epilogue
+@pytest.mark.parametrize("M,K,N,r", [(64, 256, 256, 32), (37, 96, 130, 5), (130, 512, 520, 16), (16, 64, 48, 64),
+                                     (40, 4160, 300, 32), (20, 8192, 64, 24), (33, 1024, 260, 24)])
 def test_svdq_small(qt, M, K, N, r):
     _say(f"svdq small qt={qt} M={M} K={K} N={N} r={r}")
     rng = np.random.default_rng(M + K + N + r)
