@@ -159,8 +159,13 @@ __global__ __launch_bounds__(kThreads) void small_kernel(const double *__restric
     __shared__ int flag;
     const int t = threadIdx.x;
     for (int e = t; e < sp * sp; e += kThreads) {
+        // all partials of the entry in flight at once, then summed in order
+        double v[kGramParts];
+#pragma unroll
+        for (int g = 0; g < kGramParts; ++g) v[g] = partial[(size_t)g * sp * sp + e];
         double s = 0.0;
-        for (int g = 0; g < kGramParts; ++g) s += partial[(size_t)g * sp * sp + e];
+#pragma unroll
+        for (int g = 0; g < kGramParts; ++g) s += v[g];
         A[e / sp][e % sp] = s;
     }
     __syncthreads();
