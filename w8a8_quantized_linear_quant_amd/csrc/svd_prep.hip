@@ -173,25 +173,27 @@ __global__ __launch_bounds__(kThreads) void small_kernel(const double *__restric
         double dmax = 0.0;
         for (int k = 0; k < sp; ++k) dmax = fmax(dmax, A[k][k]);
         const double tiny = 1e-13 * dmax;
-        // Cholesky, column by column (V holds R, upper)
+        // Cholesky, right-looking (V holds R, upper): step k takes the pivot,
+        // scales row k, then the whole workgroup subtracts the outer product
+        // of row k from the trailing upper triangle of A -- the same products
+        // subtracted in the same order (i ascending) as a column-by-column
+        // formulation, spread over the threads instead of one dot product
+        // per column.
         for (int e = t; e < sp * sp; e += kThreads) V[e / sp][e % sp] = 0.0;
         __syncthreads();
         for (int k = 0; k < sp; ++k) {
             if (t == 0) {
-                double d = A[k][k];
-                for (int i = 0; i < k; ++i) d -= V[i][k] * V[i][k];
+                const double d = A[k][k];
                 flag = d > tiny && d > 0.0;
                 V[k][k] = flag ? sqrt(d) : 1.0;
             }
             __syncthreads();
-            for (int j = k + 1 + t; j < sp; j += kThreads) {
-                double v = 0.0;
-                if (flag) {
-                    v = A[k][j];
-                    for (int i = 0; i < k; ++i) v -= V[i][k] * V[i][j];
-                    v /= V[k][k];
-                }
-                V[k][j] = v;
+            for (int j = k + 1 + t; j < sp; j += kThreads) V[k][j] = flag ? A[k][j] / V[k][k] : 0.0;
+            __syncthreads();
+            const int n = sp - 1 - k;  // trailing size
+            for (int e = t; e < n * n; e += kThreads) {
+                const int i = k + 1 + e / n, j = k + 1 + e % n;
+                if (i <= j) A[i][j] -= V[k][i] * V[k][j];
             }
             __syncthreads();
         }
