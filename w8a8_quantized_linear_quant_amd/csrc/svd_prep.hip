@@ -261,24 +261,26 @@ __global__ __launch_bounds__(kThreads) void small_kernel(const double *__restric
                 pp[t] = p; pq[t] = q; rc[t] = c; rs[t] = s;
             }
             __syncthreads();
-            // rows: A <- J^T A
-            for (int e = t; e < np * sp; e += kThreads) {
-                const int k = e / sp, col = e % sp;
-                const int p = pp[k], q = pq[k];
-                const double c = rc[k], s = rs[k];
-                const double ap = A[p][col], aq = A[q][col];
-                A[p][col] = c * ap - s * aq;
-                A[q][col] = s * ap + c * aq;
+            // A <- J^T A J one 2x2 block at a time: rows p, q of pair k and
+            // columns p', q' of pair l, first rotated as rows by pair k, then
+            // as columns by pair l (the pairs partition the indices, so the
+            // blocks are disjoint); and V <- V J
+            for (int e = t; e < np * np; e += kThreads) {
+                const int k = e / np, l = e % np;
+                const int p = pp[k], q = pq[k], p2 = pp[l], q2 = pq[l];
+                const double c = rc[k], s = rs[k], c2 = rc[l], s2 = rs[l];
+                const double apr = A[p][p2], aqr = A[q][p2], aps = A[p][q2], aqs = A[q][q2];
+                const double bpr = c * apr - s * aqr, bqr = s * apr + c * aqr;
+                const double bps = c * aps - s * aqs, bqs = s * aps + c * aqs;
+                A[p][p2] = c2 * bpr - s2 * bps;
+                A[p][q2] = s2 * bpr + c2 * bps;
+                A[q][p2] = c2 * bqr - s2 * bqs;
+                A[q][q2] = s2 * bqr + c2 * bqs;
             }
-            __syncthreads();
-            // columns: A <- A J, and V <- V J
             for (int e = t; e < np * sp; e += kThreads) {
                 const int k = e / sp, row = e % sp;
                 const int p = pp[k], q = pq[k];
                 const double c = rc[k], s = rs[k];
-                const double ap = A[row][p], aq = A[row][q];
-                A[row][p] = c * ap - s * aq;
-                A[row][q] = s * ap + c * aq;
                 const double vp = V[row][p], vq = V[row][q];
                 V[row][p] = c * vp - s * vq;
                 V[row][q] = s * vp + c * vq;
