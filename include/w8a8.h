@@ -205,7 +205,8 @@ w8a8_status svdq_linear(w8a8_qtype qtype, const uint16_t *x, int64_t M, int64_t 
  *   w bf16 [N, K]; workspace svdq_prepare_workspace_bytes(N, K, r) bytes
  *   (about 2 N K + 8 (N + K) s bytes).
  * Shape rules: 1 <= r <= 64, r <= N, r <= K, N % 8 == K % 8 == 0,
- * N * K <= 2^31; else W8A8_ERR_INVALID_ARG (r, iters) or W8A8_ERR_SHAPE.
+ * N, K < 2^24, N * K <= 2^31; else W8A8_ERR_INVALID_ARG (r, iters) or
+ * W8A8_ERR_SHAPE.
  */
 int64_t svdq_prepare_subspace(int64_t r);
 size_t svdq_prepare_workspace_bytes(int64_t N, int64_t K, int64_t r);

@@ -162,6 +162,7 @@ def test_svdq_prepare_rejects_and_sizes():
     assert f(*args(it=-1)) == INVALID
     assert f(*args(N=60)) == SHAPE                                  # N % 8
     assert f(*args(K=16, r=24)) == SHAPE                            # r > K
+    assert f(*args(N=1 << 24, K=64)) == SHAPE                       # N < 2^24
     assert f(*args(w=NULL)) == INVALID
     assert f(*args(om=MIS)) == ALIGN
 

@@ -58,30 +58,52 @@ __global__ __launch_bounds__(kThreads) void thin_product_kernel(const uint16_t *
     __shared__ float part[4][16][kMaxS + 1];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m0 = blockIdx.x * 16;
-    const int row = m0 + (lane & 15);
     const int lq = (lane >> 4) * 8;
     const int nsteps = (L + 31) / 32;
     const int jb = sp / 16;
     v4f acc[kMaxS / 16];
 #pragma unroll
     for (int b = 0; b < kMaxS / 16; ++b) acc[b] = v4f{0.f, 0.f, 0.f, 0.f};
-    const uint16_t zero8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (int st = wave; st < nsteps; st += 4) {
-        const int l = st * 32 + lq;
-        const bool lin = l + 8 <= L;
-        const v8bf_t av = (row < rows && lin) ? *reinterpret_cast<const v8bf_t *>(a + (size_t)row * L + l)
-                                              : __builtin_bit_cast(v8bf_t, zero8);
+    // Buffer ranges: this workgroup's rows of A, and B whole; rows past
+    // `rows` and l past L read zero (out-of-range offsets), so the loads need
+    // no branches and kU steps' loads are all in flight before their MFMAs.
+    // (sizes stay below 0x7FFFFFF0: sp <= 64 and L < 2^24, checked on the host)
+    const int rows_in = min(16, rows - m0);
+    const int a_bytes = (int)((int64_t)rows_in * L * 2), b_bytes = (int)((int64_t)sp * L * 2);
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a + (size_t)m0 * L), (short)0, a_bytes, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rh =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(bhi), (short)0, b_bytes, kBufferRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(blo ? blo : bhi), (short)0, blo ? b_bytes : 0, kBufferRsrcWord3);
+    constexpr int kU = 4;  // steps per batch of loads
+    constexpr int kOut = 0x7FFFFFF0;
+    for (int st0 = wave; st0 < nsteps; st0 += 4 * kU) {
+        v4u av[kU], h[kU][kMaxS / 16], lo[kU][kMaxS / 16];
 #pragma unroll
-        for (int b = 0; b < kMaxS / 16; ++b) {
-            if (b >= jb) break;
-            const int j = b * 16 + (lane & 15);
-            const v8bf_t h = lin ? *reinterpret_cast<const v8bf_t *>(bhi + (size_t)j * L + l)
-                                 : __builtin_bit_cast(v8bf_t, zero8);
-            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, h, acc[b], 0, 0, 0);
-            if (blo) {
-                const v8bf_t lo = lin ? *reinterpret_cast<const v8bf_t *>(blo + (size_t)j * L + l)
-                                      : __builtin_bit_cast(v8bf_t, zero8);
-                acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, lo, acc[b], 0, 0, 0);
+        for (int u = 0; u < kU; ++u) {
+            const int l = (st0 + 4 * u) * 32 + lq;
+            const bool lin = l + 8 <= L;
+            av[u] = __builtin_bit_cast(
+                v4u, __builtin_amdgcn_raw_buffer_load_b128(ra, lin ? ((lane & 15) * L + l) * 2 : kOut, 0, 0));
+#pragma unroll
+            for (int b = 0; b < kMaxS / 16; ++b) {
+                const int j = b * 16 + (lane & 15);
+                const int off = lin && b < jb ? (j * L + l) * 2 : kOut;
+                h[u][b] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rh, off, 0, 0));
+                lo[u][b] = __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(rl, off, 0, 0));
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < kU; ++u) {
+            const v8bf_t x = __builtin_bit_cast(v8bf_t, av[u]);
+#pragma unroll
+            for (int b = 0; b < kMaxS / 16; ++b) {
+                if (b >= jb) break;
+                acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, __builtin_bit_cast(v8bf_t, h[u][b]), acc[b], 0, 0, 0);
+                if (blo)
+                    acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, __builtin_bit_cast(v8bf_t, lo[u][b]), acc[b],
+                                                                     0, 0, 0);
             }
         }
     }
@@ -466,7 +488,7 @@ extern "C" w8a8_status svdq_prepare(const uint16_t *w, int64_t N, int64_t K, int
     using namespace w8a8;
     if (N < 1 || K < 1 || r < 1 || r > kMaxS || iters < 0 || iters > 16) return W8A8_ERR_INVALID_ARG;
     if (r > N || r > K) return W8A8_ERR_SHAPE;
-    if (N % 8 != 0 || K % 8 != 0 || N > (1 << 24) || K > (1 << 24) || N * K > ((int64_t)1 << 31))
+    if (N % 8 != 0 || K % 8 != 0 || N >= (1 << 24) || K >= (1 << 24) || N * K > ((int64_t)1 << 31))
         return W8A8_ERR_SHAPE;
     if (!w || !omega || !l1 || !l2 || !residual || !sigma || !workspace) return W8A8_ERR_INVALID_ARG;
     if (!aligned16(w) || !aligned16(omega) || !aligned16(l1) || !aligned16(l2) || !aligned16(residual) ||
