@@ -124,39 +124,58 @@ __global__ __launch_bounds__(kThreads) void thin_product_kernel(const uint16_t *
 
 // ---------------------------------------------------------------- Gram partials
 // partial[g][i][j] = sum over rows of chunk g of C[row, i] C[row, j] (f64),
-// chunk g = rows [g * chunk, (g + 1) * chunk).
+// chunk g = rows [g * chunk, (g + 1) * chunk).  Thread t owns the bs x bs block
+// of entries (bs = sp / 16) at block row t / 16, block column t % 16; a tile
+// of 64 rows sits in LDS as f64, and each entry is summed over the tile's rows
+// in order, then added to the entry's running sum (the products are exact in
+// f64, one rounding per addition).
 __global__ __launch_bounds__(kThreads) void gram_partial_kernel(const float *__restrict__ c, int rows, int sp,
                                                                 int chunk, double *__restrict__ partial) {
-    __shared__ float tile[64][kMaxS + 1];
-    const int g = blockIdx.x;
+    __shared__ double tile[64][kMaxS + 1];
+    constexpr int kB = kMaxS / 16;  // largest block edge
+    const int g = blockIdx.x, t = threadIdx.x;
+    const int bs = sp / 16, i0 = (t / 16) * bs, j0 = (t % 16) * bs;
     const int r_begin = g * chunk, r_end = min(rows, r_begin + chunk);
-    constexpr int kMaxEnt = kMaxS * kMaxS / kThreads;  // 16 entries per thread at sp = 64
-    double acc[kMaxEnt];
+    double acc[kB][kB];
 #pragma unroll
-    for (int e = 0; e < kMaxEnt; ++e) acc[e] = 0.0;
+    for (int a = 0; a < kB; ++a)
+#pragma unroll
+        for (int b = 0; b < kB; ++b) acc[a][b] = 0.0;
     for (int r0 = r_begin; r0 < r_end; r0 += 64) {
         const int nr = min(64, r_end - r0);
         __syncthreads();
-        for (int idx = threadIdx.x; idx < 64 * sp; idx += kThreads) {
+        for (int idx = t; idx < 64 * sp; idx += kThreads) {
             const int rr = idx / sp, j = idx % sp;
-            tile[rr][j] = rr < nr ? c[(size_t)(r0 + rr) * sp + j] : 0.0f;
+            tile[rr][j] = rr < nr ? (double)c[(size_t)(r0 + rr) * sp + j] : 0.0;
         }
         __syncthreads();
+        double s[kB][kB];
 #pragma unroll
-        for (int e = 0; e < kMaxEnt; ++e) {
-            const int ent = threadIdx.x + e * kThreads;
-            if (ent >= sp * sp) break;
-            const int i = ent / sp, j = ent % sp;
-            double s = 0.0;
-            for (int rr = 0; rr < nr; ++rr) s += (double)tile[rr][i] * (double)tile[rr][j];
-            acc[e] += s;
+        for (int a = 0; a < kB; ++a)
+#pragma unroll
+            for (int b = 0; b < kB; ++b) s[a][b] = 0.0;
+        for (int rr = 0; rr < nr; ++rr) {
+            double xi[kB], xj[kB];
+#pragma unroll
+            for (int a = 0; a < kB; ++a) {
+                xi[a] = a < bs ? tile[rr][i0 + a] : 0.0;
+                xj[a] = a < bs ? tile[rr][j0 + a] : 0.0;
+            }
+#pragma unroll
+            for (int a = 0; a < kB; ++a)
+#pragma unroll
+                for (int b = 0; b < kB; ++b) s[a][b] += xi[a] * xj[b];
         }
+#pragma unroll
+        for (int a = 0; a < kB; ++a)
+#pragma unroll
+            for (int b = 0; b < kB; ++b) acc[a][b] += s[a][b];
     }
 #pragma unroll
-    for (int e = 0; e < kMaxEnt; ++e) {
-        const int ent = threadIdx.x + e * kThreads;
-        if (ent < sp * sp) partial[(size_t)g * sp * sp + ent] = acc[e];
-    }
+    for (int a = 0; a < kB; ++a)
+#pragma unroll
+        for (int b = 0; b < kB; ++b)
+            if (a < bs && b < bs) partial[(size_t)g * sp * sp + (size_t)(i0 + a) * sp + j0 + b] = acc[a][b];
 }
 
 // ---------------------------------------------------------------- s x s work
