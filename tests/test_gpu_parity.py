@@ -508,6 +508,34 @@ def test_gguf_a8_requant_exact_ties(qt):
     assert_equal(bytes_host(wq), ref_q, "codes")
 
 
+@pytest.mark.parametrize("qt", [INT8, FP8])
+def test_gguf_a8_requant_signed_scales(qt):
+    """Blocks with negative, zero and negative-zero scales d and many zero
+    codes: q d is -0 for q = 0 under a negative d, which e4m3 codes as 0x80
+    (its own code, unlike +0), and |q d| must take |d|."""
+    rng = np.random.default_rng(11)
+    N, K = 5, 160
+    nb = K // 32
+    d = (rng.uniform(0.001, 0.02, (N, nb)) * rng.choice([-1.0, 1.0], (N, nb))).astype(np.float16)
+    d[0, 1] = np.float16(0.0)
+    d[1, 2] = np.float16(-0.0)
+    d[2] = -np.abs(d[2])                                     # a row with only negative scales
+    q = rng.integers(-127, 128, (N, nb, 32))
+    q[rng.random((N, nb, 32)) < 0.3] = 0
+    q[3, :, :] = 0                                           # an all-zero row under mixed signs
+    blob = np.empty((N * nb, 34), np.uint8)
+    blob[:, :2] = d.reshape(-1).view(np.uint8).reshape(-1, 2)
+    blob[:, 2:] = q.reshape(-1, 32).astype(np.int8).view(np.uint8)
+    blob = blob.ravel()
+    wq, s = W8.gguf_a8_requant_q8_0(torch.from_numpy(blob).cuda(), N, K, qtype=qt)
+    torch.cuda.synchronize()
+    ref_q, ref_s = oracle.gguf_a8_requant_q8_0(qt, blob, N, K)
+    if qt == FP8:
+        assert (ref_q == 0x80).any()                         # the case is exercised
+    assert_equal(s.cpu().numpy().view(np.uint32), ref_s.view(np.uint32), "scales")
+    assert_equal(bytes_host(wq), ref_q, "codes")
+
+
 def test_gguf_a8_requant_full():
     _say("gguf a8 requant N=12288 K=3072 full")
     d = workloads.gguf()

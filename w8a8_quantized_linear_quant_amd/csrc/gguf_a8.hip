@@ -74,30 +74,46 @@ __global__ __launch_bounds__(kThreads) void gguf_a8_requant_row_kernel(const uin
         const uint32_t vlast = a0 + 16u * (nvec - 1);
         if (vlast + 16u > total_bytes && lane < 16)
             st[16 * (nvec - 1) + lane] = __builtin_amdgcn_raw_buffer_load_b8(rs, vlast + lane, 0, 0);
-        // values of this lane's 4 codes of block b (b < nb)
+        // Values q d of this lane's 4 codes of block b (b < nb).  For int8
+        // each code byte is flipped to q + 128 in [0, 255] (one XOR for the
+        // 4), which converts as an unsigned byte; fma(q + 128, d, -128 d)
+        // then gives q d exactly: both products fit in 19 bits and their
+        // difference is q d itself, an f32 value.  Only the sign of a zero
+        // can differ (+0 for q = 0, d < 0), which the int8 code ignores; e4m3
+        // codes -0 and +0 apart, so that path multiplies the signed code.
         auto block_vals = [&](int b, float *v) {
             const uint8_t *bp = st + off + b * 34;
             const uint32_t dbits = *reinterpret_cast<const uint16_t *>(bp);
             const uint32_t lo = *reinterpret_cast<const uint16_t *>(bp + 2 + 4 * part);
             const uint32_t hi = *reinterpret_cast<const uint16_t *>(bp + 4 + 4 * part);
             const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)dbits);
-            const uint32_t w = lo | (hi << 16);
+            if constexpr (QT == W8A8_INT8) {
+                const float nd = -128.0f * d;
+                const uint32_t w = (lo | (hi << 16)) ^ 0x80808080u;  // q + 128 per byte
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = (float)(int8_t)(w >> (8 * i)) * d;  // exact in f32
+                for (int i = 0; i < 4; ++i) v[i] = fmaf((float)((w >> (8 * i)) & 0xFFu), d, nd);
+            } else {
+                const uint32_t w = lo | (hi << 16);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = (float)(int8_t)(w >> (8 * i)) * d;  // exact in f32
+            }
         };
         // |q d| of this lane's 4 codes of block b, maximized: every product is
-        // exact in f32 (8-bit q, 11-bit d), so the largest is max|q| * |d|.
+        // exact in f32 (8-bit q, 11-bit d), so the largest is max|q| * |d|,
+        // and max|q| = max(max(q + 128) - 128, 128 - min(q + 128)).
         auto block_absmax = [&](int b) {
             const uint8_t *bp = st + off + b * 34;
             const uint32_t dbits = *reinterpret_cast<const uint16_t *>(bp);
             const uint32_t lo = *reinterpret_cast<const uint16_t *>(bp + 2 + 4 * part);
             const uint32_t hi = *reinterpret_cast<const uint16_t *>(bp + 4 + 4 * part);
             const float d = (float)__builtin_bit_cast(_Float16, (uint16_t)dbits);
-            const uint32_t w = lo | (hi << 16);
-            float m = 0.0f;
+            const uint32_t w = (lo | (hi << 16)) ^ 0x80808080u;  // q + 128 per byte
+            float u[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf((float)(int8_t)(w >> (8 * i))));
-            return m * fabsf(d);
+            for (int i = 0; i < 4; ++i) u[i] = (float)((w >> (8 * i)) & 0xFFu);
+            const float hi_u = fmaxf(fmaxf(u[0], u[1]), fmaxf(u[2], u[3]));
+            const float lo_u = fminf(fminf(u[0], u[1]), fminf(u[2], u[3]));
+            return fmaxf(hi_u - 128.0f, 128.0f - lo_u) * fabsf(d);
         };
         // Row absmax (non-negative floats order like their bit patterns), 32
         // blocks (4 steps of 8) per iteration with their LDS reads issued
@@ -139,7 +155,9 @@ __global__ __launch_bounds__(kThreads) void gguf_a8_requant_row_kernel(const uin
                     pk = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], pk, true);
                     word = (uint32_t)pk;
                 }
-                if (b < nb) *reinterpret_cast<uint32_t *>(st + b * 32 + 4 * part) = word;
+                // past the row's last block a lane rewrites that block's own
+                // word with the same value (its index was clamped above)
+                *reinterpret_cast<uint32_t *>(st + min(b, nb - 1) * 32 + 4 * part) = word;
             }
         }
         // the row's codes leave as 16-byte stores, 4 LDS reads per lane at a time
