@@ -484,6 +484,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                 bias2[nb][j] = b;
             }
         constexpr bool kLr32 = EPI == kEpiLowRank32;
+        constexpr bool kLrBatch = kLr32 && kInt8;
         uint8_t *ub = buf(std::integral_constant<int, NST - 1>{});
         uint8_t *lb = buf(std::integral_constant<int, NST - 2>{});
         const int half_bytes = 256 * p.rp * 2;
@@ -515,19 +516,62 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_ptr_t)(ub + half_bytes + off), 16, off + el * 16, 0,
                                                          0, 0);
             }
+            if constexpr (kLrBatch) {
+                // int8: scale the accumulators in place while the operands land
+#pragma unroll
+                for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb) {
+                        v16f t;
+#pragma unroll
+                        for (int e = 0; e < 16; ++e) t[e] = (float)acc[nb][mb][e] * tm[mb];
+                        acc[nb][mb] = __builtin_bit_cast(acc_t, t);
+                    }
+            }
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             asm volatile("s_barrier" ::: "memory");
         }
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
+            if constexpr (kLrBatch) {
+                // u . l2^T of the 4 blocks of this block row from the staged
+                // rows, the MFMAs interleaved over the blocks so that they
+                // issue back to back rather than each waiting on the last
+                const int urow = wm * 128 + mb * 32 + erow;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    if (ks * 16 >= p.rp) break;
+                    const int j0 = ks * 16 + ehalf * 8;
+                    v8bf a[4];
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb)
+                        a[nb] = *reinterpret_cast<const v8bf *>(lb + ((wn * 128 + nb * 32 + erow) * p.r + j0) * 2);
+                    const v8bf uh = *reinterpret_cast<const v8bf *>(ub + (urow * p.rp + j0) * 2);
+                    const v8bf ul = *reinterpret_cast<const v8bf *>(ub + half_bytes + (urow * p.rp + j0) * 2);
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb)
+                        acc[nb][mb] = __builtin_bit_cast(acc_t, __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            a[nb], uh, __builtin_bit_cast(v16f, acc[nb][mb]), 0, 0, 0));
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb)
+                        acc[nb][mb] = __builtin_bit_cast(acc_t, __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                            a[nb], ul, __builtin_bit_cast(v16f, acc[nb][mb]), 0, 0, 0));
+                }
+            }
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) {
                 v16f v;
+                if constexpr (kLrBatch) {
+                    v = __builtin_bit_cast(v16f, acc[nb][mb]);
+                } else {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) v[e] = (float)acc[nb][mb][e] * tm[mb];
+                    for (int e = 0; e < 16; ++e) v[e] = (float)acc[nb][mb][e] * tm[mb];
+                }
                 if constexpr (EPI == kEpiLowRank) v = low_rank_add(p, v, nw + nb * 32, mw + mb * 32, erow, ehalf);
-                if constexpr (kLr32) {
-                    // u . l2^T of this block from the staged rows
+                if constexpr (kLr32 && !kLrBatch) {
+                    // e4m3: u . l2^T of this block from the staged rows (the
+                    // interleaved form above needs more registers than this
+                    // instantiation has, and was slower)
                     const int urow = wm * 128 + mb * 32 + erow, lrow2 = wn * 128 + nb * 32 + erow;
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks) {
