@@ -10,20 +10,13 @@
 // workspace; kernel 2 lets every workgroup re-reduce those partials (a few KB
 // from L2, no atomics, no clearing) and quantize its share; kernel 3, only if
 // requested, writes the transposed code copy [K, N] through 64x64 LDS tiles.
-#include "common.hpp"
+#include "act_quant.hpp"
 
 namespace w8a8 {
 namespace {
 
 constexpr int kPartials = 1024;  // workgroups of the max pass = partial count
 constexpr int kThreads = 256;
-
-typedef unsigned short us2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
-    us2 x = __builtin_bit_cast(us2, a), y = __builtin_bit_cast(us2, b);
-    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, y));
-}
 
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t *red) {
     v = wave_max_u32(v);
@@ -53,37 +46,6 @@ __global__ __launch_bounds__(kThreads) void weight_absmax_kernel(const uint16_t 
 }
 
 template <int QT>
-__device__ __forceinline__ uint2 codes8(v4u d, float s) {
-    // Weights are quantized once: the plain IEEE division is used.
-    uint32_t out[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        float v[4];
-#pragma unroll
-        for (int e = 0; e < 2; ++e) {
-            v[2 * e] = __uint_as_float(d[2 * h + e] << 16) / s;
-            v[2 * e + 1] = __uint_as_float(d[2 * h + e] & 0xFFFF0000u) / s;
-        }
-        if constexpr (QT == W8A8_INT8) {
-            uint32_t word = 0;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                int q = (int)__builtin_rintf(__builtin_amdgcn_fmed3f(v[i], -128.0f, 127.0f));
-                word |= ((uint32_t)q & 0xFFu) << (8 * i);
-            }
-            out[h] = word;
-        } else {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = __builtin_amdgcn_fmed3f(v[i], -448.0f, 448.0f);
-            int pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-            pk = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], pk, true);
-            out[h] = (uint32_t)pk;
-        }
-    }
-    return make_uint2(out[0], out[1]);
-}
-
-template <int QT>
 __global__ __launch_bounds__(kThreads) void weight_quant_kernel(const uint16_t *__restrict__ w, int64_t nchunks,
                                                                 const uint32_t *__restrict__ partial, int npartial,
                                                                 uint8_t *__restrict__ wq, float *__restrict__ w_scale) {
@@ -94,10 +56,23 @@ __global__ __launch_bounds__(kThreads) void weight_quant_kernel(const uint16_t *
     m = block_max_u32(m, red);
     const float s = absmax_scale(bf16_bits_to_f32(m), kQmax);
     if (blockIdx.x == 0 && threadIdx.x == 0) w_scale[0] = s;
+    // The codes are the act-quant's (quantize8): its one-correction quotient
+    // equals the IEEE quotient for every bf16 value and every scale derived
+    // from a bf16 absmax, which this scale is.
+    const float r = 1.0f / s;
     const v4u *p = reinterpret_cast<const v4u *>(w);
     uint2 *q = reinterpret_cast<uint2 *>(wq);
-    for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < nchunks; c += (int64_t)gridDim.x * kThreads)
-        q[c] = codes8<QT>(p[c], s);
+    const int64_t stride = (int64_t)gridDim.x * kThreads;
+    int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    // four chunks per thread with their loads issued together
+    for (; c + 3 * stride < nchunks; c += 4 * stride) {
+        v4u d[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d[j] = p[c + j * stride];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) q[c + j * stride] = quantize8<QT>(d[j], s, r);
+    }
+    for (; c < nchunks; c += stride) q[c] = quantize8<QT>(p[c], s, r);
 }
 
 // wq [N, K] -> wq_t [K, N] bytes, 64x64 tiles through LDS.
