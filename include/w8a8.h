@@ -178,9 +178,18 @@ size_t svdq_workspace_bytes(int64_t M, int64_t r);
  *   projection, nn.Linear layout); l2 bf16 [N, r] (up-projection); bias bf16
  *   [N] or NULL; y bf16 [M, N]; xq_out codes [M, K]; x_scale_out f32 [M];
  *   workspace svdq_workspace_bytes(M, r) bytes.
- * Three launches: the row-wise act-quant, the down-projection (bf16 MFMA,
- * u written as a hi/lo pair of bf16 halves so it keeps ~16 bits), then the
- * 8-bit product whose epilogue adds the up-projection on the bf16 MFMA.
+ * Factor layout: both factors are stored as nn.Linear weights [out, in], the
+ * layout of a LoRA pair (down [r, K], up [N, r]); in the matrix-product form
+ * y = X A B with A [K, r], B [r, N] that is l1 = A^T and l2 = B^T.  Rows of l1
+ * run along K like the rows of X and W, so the down-projection streams them
+ * with the same 16-byte loads; rows of l2 hold the r factors of one output
+ * column contiguously, which the epilogue reads per column.
+ * Launches: for K <= 4096 and r <= 32, two -- one kernel reads X once for
+ * both the row-wise quantization and the down-projection (bf16 MFMA, u
+ * written as a hi/lo pair of bf16 halves so it keeps ~16 bits), then the
+ * 8-bit product whose epilogue adds the up-projection on the bf16 MFMA;
+ * otherwise three -- the row-wise act-quant, the down-projection, the
+ * product.
  * Shape rules: as w8a8_linear (K % 16 == 0); 1 <= r <= 64, else
  * W8A8_ERR_INVALID_ARG.
  */

@@ -46,6 +46,22 @@ def assert_bf16_close(got_bits, ref_bits, what=""):
     return float((err / (np.abs(ref) + 1e-30)).max())
 
 
+FROB_REL = 1e-3
+
+
+def assert_frobenius(got_bits, ref_bits, what="", tol=FROB_REL):
+    """Relative Frobenius error ||got - ref||_F / ||ref||_F <= tol in f64 (the
+    bar of the e4m3 products, where both sides use identical e4m3 codes)."""
+    got = bf16_to_f64(got_bits)
+    ref = bf16_to_f64(ref_bits)
+    assert got.shape == ref.shape
+    den = float(np.sqrt(np.sum(ref * ref)))
+    num = float(np.sqrt(np.sum((got - ref) ** 2)))
+    rel = num / den if den > 0 else num
+    assert rel <= tol, f"{what}: relative Frobenius error {rel:.3e} > {tol:g}"
+    return rel
+
+
 def assert_equal(got, ref, what=""):
     got = np.asarray(got)
     ref = np.asarray(ref)

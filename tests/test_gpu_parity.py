@@ -9,8 +9,8 @@ import torch
 
 import oracle
 import workloads
-from helpers import (assert_bf16_close, assert_equal, bf16_dev, bf16_host, bytes_host, codes_dev, f32_dev,
-                     sample_rows)
+from helpers import (assert_bf16_close, assert_equal, assert_frobenius, bf16_dev, bf16_host, bytes_host, codes_dev,
+                     f32_dev, sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,7 +37,14 @@ INT8, FP8 = oracle.INT8, oracle.FP8_E4M3
 # ------------------------------------------------------------ act quant
 def _act_quant_check(x_bits, qt, ldq=None, rows=None, what=""):
     M, K = x_bits.shape
-    xq, sx = W8.w8a8_quant_act_rowwise(bf16_dev(x_bits), qtype=qt, ldq=ldq)
+    if K % 8:
+        # rows must start on 16-byte boundaries: a [:, :K] view of padded rows
+        xp = np.zeros((M, K + (-K) % 8), np.uint16)
+        xp[:, :K] = x_bits
+        xd = bf16_dev(xp)[:, :K]
+    else:
+        xd = bf16_dev(x_bits)
+    xq, sx = W8.w8a8_quant_act_rowwise(xd, qtype=qt, ldq=ldq)
     torch.cuda.synchronize()
     got_q, got_s = bytes_host(xq), sx.cpu().numpy()
     sel = np.arange(M) if rows is None else rows
@@ -83,9 +90,14 @@ def test_act_quant_every_bf16_value(qt, qmax):
     # one row per scale 2^e: [qmax * 2^e, every bf16 value v with |v| <= qmax * 2^e]
     _say(f"act_quant every bf16 value qt={qt}")
     allv = workloads.bf16_bits_to_f32(np.arange(65536, dtype=np.uint32).astype(np.uint16))
+    # Powers of two give exact reciprocals; the absmax values qmax (1 + k/128) 2^e
+    # (rounded to bf16) give scales whose reciprocal is inexact, where the
+    # kernels' corrected quotient has to reproduce the IEEE division.
     rows = []
-    for e in (-20, -3, 0, 5):
-        lim = np.float32(qmax * 2.0 ** e)
+    lims = [qmax * 2.0 ** e for e in (-20, -3, 0, 5)]
+    lims += [qmax * (1 + k / 128) * 2.0 ** e for k, e in ((1, 0), (37, -3), (85, 2), (127, -9), (51, 7))]
+    for lim in lims:
+        lim = workloads.bf16_bits_to_f32(workloads.f32_to_bf16_bits(np.array([lim], np.float32)))[0]
         v = allv[np.isfinite(allv) & (np.abs(allv) <= lim)]
         rows.append(np.concatenate([[lim], v]))
     K = max(len(r) for r in rows)
@@ -232,7 +244,10 @@ def test_linear_tiny(qt, with_bias):
     got = _gpu_linear(d["x"], d["w"], bias, qt)
     xq, sx = oracle.quant_act_rowwise(qt, d["x"])
     wq, _, sw = oracle.quant_weight_tensorwise(qt, d["w"])
-    assert_bf16_close(got, oracle.linear(qt, xq, sx, wq, sw, bias), "tiny linear")
+    ref = oracle.linear(qt, xq, sx, wq, sw, bias)
+    assert_bf16_close(got, ref, "tiny linear")
+    if qt == FP8:
+        assert_frobenius(got, ref, "tiny e4m3 linear")
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 24, 16), (5, 200, 48), (257, 300, 272), (130, 64, 1040)])
@@ -246,7 +261,10 @@ def test_linear_ragged(M, N, K):
         got = _gpu_linear(x, w, b, qt)
         xq, sx = oracle.quant_act_rowwise(qt, x)
         wq, _, sw = oracle.quant_weight_tensorwise(qt, w)
-        assert_bf16_close(got, oracle.linear(qt, xq, sx, wq, sw, b), f"ragged qt={qt}")
+        ref = oracle.linear(qt, xq, sx, wq, sw, b)
+        assert_bf16_close(got, ref, f"ragged qt={qt}")
+        if qt == FP8:
+            assert_frobenius(got, ref, "ragged e4m3 linear")
 
 
 @pytest.mark.parametrize("which", ["w1", "w2"])
@@ -281,6 +299,7 @@ def test_linear_headline_full_sampled():
     assert_equal(bytes_host(xq)[rows], rxq, "activation codes")
     assert_equal(sw.cpu().numpy().reshape(-1).view(np.uint32),
                  np.atleast_1d(np.float32(rsw)).view(np.uint32), "weight scale")
+    assert_equal(bytes_host(wq), rwq, "weight codes [12288, 3072]")
     assert_bf16_close(bf16_host(y)[rows], oracle.linear(INT8, rxq, rsx, rwq, rsw, b), "headline Y")
 
 
@@ -315,13 +334,23 @@ def test_fp8_step_forward_and_backward_sampled():
     rows = sample_rows(M, 4)
     cols = np.unique(np.concatenate([np.arange(0, N, 97), [N - 1]]))
     kcols = np.unique(np.concatenate([np.arange(0, K, 29), [K - 1]]))
-    owq, _, osw = oracle.quant_weight_tensorwise(FP8, w)
+    owq, owqt, osw = oracle.quant_weight_tensorwise(FP8, w, transposed=True)
+    assert_equal(sw.cpu().numpy().reshape(-1).view(np.uint32), np.atleast_1d(np.float32(osw)).view(np.uint32),
+                 "e4m3 weight scale")
+    assert_equal(bytes_host(wq), owq, "e4m3 weight codes [12288, 3072]")
+    assert_equal(bytes_host(wqt), owqt, "e4m3 transposed weight codes [3072, 12288]")
     oxq, osx = oracle.quant_act_rowwise(FP8, x[rows])
+    assert_equal(bytes_host(xq)[rows], oxq, "e4m3 activation codes")
     ref_y = oracle.linear(FP8, oxq, osx, owq[cols], osw)
-    assert_bf16_close(bf16_host(y)[rows][:, cols], ref_y, "fp8 forward")
+    got_y = bf16_host(y)[rows][:, cols]
+    assert_bf16_close(got_y, ref_y, "fp8 forward")
+    assert_frobenius(got_y, ref_y, "fp8 forward")
     odyq, osdy = oracle.quant_act_rowwise(FP8, dy[rows])
+    assert_equal(bytes_host(dyq)[rows], odyq, "e4m3 dY codes")
     ref_dx = oracle.linear_backward_dx(FP8, odyq, osdy, np.ascontiguousarray(owq[:, kcols]), osw)
-    assert_bf16_close(bf16_host(dx)[rows][:, kcols], ref_dx, "fp8 dX")
+    got_dx = bf16_host(dx)[rows][:, kcols]
+    assert_bf16_close(got_dx, ref_dx, "fp8 dX")
+    assert_frobenius(got_dx, ref_dx, "fp8 dX")
 
 
 @pytest.mark.parametrize("qt", [INT8, FP8])
@@ -340,7 +369,10 @@ def test_backward_dx_ragged(qt, M, N, K):
     owq, owqt, osw = oracle.quant_weight_tensorwise(qt, w, transposed=True)
     assert_equal(bytes_host(wqt), owqt, "transposed codes")
     odyq, osdy = oracle.quant_act_rowwise(qt, dy)
-    assert_bf16_close(bf16_host(dx), oracle.linear_backward_dx(qt, odyq, osdy, owq, osw), f"dX qt={qt}")
+    ref = oracle.linear_backward_dx(qt, odyq, osdy, owq, osw)
+    assert_bf16_close(bf16_host(dx), ref, f"dX qt={qt}")
+    if qt == FP8:
+        assert_frobenius(bf16_host(dx), ref, "e4m3 dX ragged")
 
 
 def test_int8_step_backward_sampled():
@@ -355,7 +387,9 @@ def test_int8_step_backward_sampled():
     torch.cuda.synchronize()
     rows = sample_rows(M, 4)
     kcols = np.unique(np.concatenate([np.arange(0, K, 29), [K - 1]]))
-    owq, _, osw = oracle.quant_weight_tensorwise(INT8, w)
+    owq, owqt, osw = oracle.quant_weight_tensorwise(INT8, w, transposed=True)
+    assert_equal(bytes_host(wq), owq, "int8 weight codes [12288, 3072]")
+    assert_equal(bytes_host(wqt), owqt, "int8 transposed weight codes [3072, 12288]")
     odyq, osdy = oracle.quant_act_rowwise(INT8, dy[rows])
     ref_dx = oracle.linear_backward_dx(INT8, odyq, osdy, np.ascontiguousarray(owq[:, kcols]), osw)
     assert_bf16_close(bf16_host(dx)[rows][:, kcols], ref_dx, "int8 dX")
@@ -383,6 +417,8 @@ def test_svdq_small(qt, M, K, N, r):
     assert_equal(bytes_host(xq), ref_xq, "svdq codes")
     assert_equal(sx.cpu().numpy().view(np.uint32), ref_sx.view(np.uint32), "svdq scales")
     assert_bf16_close(bf16_host(y), ref_y, "svdq y")
+    if qt == FP8:
+        assert_frobenius(bf16_host(y), ref_y, "svdq e4m3 y")
 
 
 @pytest.mark.parametrize("qt", [INT8, FP8])
@@ -406,6 +442,8 @@ def test_svdq_multi_tile(qt, K, r):
     orq, _, osr = oracle.quant_weight_tensorwise(qt, res)
     ref_y, _, _ = oracle.svdq_linear(qt, x[rows], orq, osr, l1, l2, b)
     assert_bf16_close(bf16_host(y)[rows], ref_y, "svdq y, several tiles per workgroup")
+    if qt == FP8:
+        assert_frobenius(bf16_host(y)[rows], ref_y, "svdq e4m3 y, several tiles per workgroup")
 
 
 def test_svdq_full_sampled():
@@ -453,6 +491,26 @@ def test_q8_0_exact_ties():
     blob = W8.q8_0_quantize(f32_dev(v))
     torch.cuda.synchronize()
     assert_equal(bytes_host(blob), oracle.q8_0_quantize(v), "q8_0 bytes on ties")
+
+
+def test_q8_0_f32_scale_block():
+    """The golden block whose codes tell the page's reading (codes from the f32
+    scale, quotient rounded to f32) from the f16-scale and unrounded-quotient
+    readings, repeated at power-of-two magnitudes (the same codes)."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "q8_0_f32_scale_block.json")) as f:
+        g = json.load(f)
+    base = np.zeros(32, np.float64)
+    for i, (num, den) in enumerate(g["values_num_den"]):
+        base[i] = num / den
+    v = np.concatenate([base * 2.0 ** e for e in (0, -7, 5, -20, 12)] + [base[:7]]).astype(np.float32)
+    blob = W8.q8_0_quantize(f32_dev(v))
+    torch.cuda.synchronize()
+    got = bytes_host(blob)
+    assert_equal(got, oracle.q8_0_quantize(v), "q8_0 bytes of the f32-scale block")
+    for b in range(5):
+        assert got[34 * b + 2: 34 * b + 10].view(np.int8).tolist() == g["codes_first8"]
 
 
 def test_q8_0_full_config():
@@ -572,6 +630,8 @@ def test_gguf_a8_linear(qt, M, N, K):
     b = workloads.normal_bf16(rng, (N,), 0.02) if M % 2 else None
     got, ref = _gguf_chain(x, blob, N, K, b, qt)
     assert_bf16_close(got, ref, f"gguf a8 linear qt={qt}")
+    if qt == FP8:
+        assert_frobenius(got, ref, "gguf a8 float linear")
 
 
 def test_gguf_a8_linear_full_sampled():
@@ -581,6 +641,8 @@ def test_gguf_a8_linear_full_sampled():
     for qt in (INT8, FP8):
         got, ref = _gguf_chain(d["x"], d["w_blocks"], d["N"], d["K"], d["bias"], qt, rows=rows)
         assert_bf16_close(got, ref, f"gguf full qt={qt}")
+        if qt == FP8:
+            assert_frobenius(got, ref, "gguf a8 float linear, full size")
 
 
 # ------------------------------------------------------------ SVDQuant preparation

@@ -3,6 +3,7 @@ a worked example, the page's size formulas, invariants and the f16 bound.
 CPU only."""
 import json
 import os
+from fractions import Fraction
 
 import numpy as np
 
@@ -73,17 +74,42 @@ def test_q8_0_invariants_and_f16_bound():
         assert np.array_equal(y, (codes.astype(np.float64) * dd[:, None]).ravel()[:n].astype(np.float32))
 
 
-def test_q8_0_zero_block_and_scale_not_exact_in_f16():
+def test_q8_0_zero_block():
     x = np.zeros(64, np.float32)
-    x[32] = 1.0                     # block 1: s = 1/127, not exact in f16
+    x[32] = 1.0
     blob = oracle.q8_0_quantize(x)
     assert blob[0] == 0 and blob[1] == 0 and not blob[2:34].any()    # f16(1e-10) = 0
-    d = np.array([int(blob[34]) | (int(blob[35]) << 8)], np.uint16)
-    assert d[0] == np.float16(np.float32(1.0) / np.float32(127.0)).view(np.uint16)
     y = oracle.q8_0_dequantize(blob, 64)
-    # codes come from the f32 scale (1.0 -> 127); dequantize uses the f16 scale
-    assert y[32] == np.float32(127.0 * float(d.view(np.float16)[0]))
-    assert y[32] != np.float32(1.0)
+    assert not y[:32].any()
+
+
+def _f32_scale_block():
+    g = _gold("q8_0_f32_scale_block.json")
+    x = np.zeros(g["n"], np.float32)
+    for i, (num, den) in enumerate(g["values_num_den"]):
+        x[i] = np.float32(num / den)
+        assert Fraction(float(x[i])) == Fraction(num, den)     # every value exact in f32
+    return g, x
+
+
+def test_q8_0_codes_from_the_f32_scale():
+    """Codes come from the f32 block scale, the quotient rounded to f32 first
+    (Q8_0::quantize divides by the f32 scale; f16 only on export).  Each of the
+    two other readings changes at least one code of this block."""
+    g, x = _f32_scale_block()
+    blob = oracle.q8_0_quantize(x)
+    assert blob.size == 34
+    assert f"{int(blob[0]) | (int(blob[1]) << 8):04X}" == g["scale_f16_hex"]
+    s = np.float32(1.0) / np.float32(127.0)
+    assert f"{int(s.view(np.uint32)):08X}" == g["scale_f32_hex"]
+    codes = blob[2:34].view(np.int8)
+    assert codes[:8].tolist() == g["codes_first8"]
+    assert not codes[8:].any()
+    assert g["codes_first8"] != g["codes_if_scale_were_f16"]
+    assert g["codes_first8"] != g["codes_if_quotient_unrounded"]
+    y = oracle.q8_0_dequantize(blob, g["n"])
+    want = [Fraction(a, b) for a, b in g["dequantized_first8_num_den"]]
+    assert [Fraction(float(v)) for v in y[:8]] == want
 
 
 def test_q8_0_outlier_vector_sample():

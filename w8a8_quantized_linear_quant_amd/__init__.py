@@ -209,12 +209,13 @@ def w8a8_quant_act_rowwise(x, qtype=INT8, ldq=None, out=None, scale=None):
     if x.dim() != 2 or x.stride(1) != 1:
         raise ValueError("x must be 2-D with unit column stride")
     M, K = x.shape
-    if M > 0 and (x.stride(0) % 8 != 0 or x.data_ptr() % 16 != 0):
-        # rows must start on 16-byte boundaries: copy into a padded buffer
-        padded = torch.zeros((M, K + (-K) % 8), dtype=x.dtype, device=x.device)
-        padded[:, :K] = x
-        x = padded
-    ldx = x.stride(0) if M > 1 else K + (-K) % 8
+    ldx = x.stride(0)
+    if M > 0 and (ldx % 8 != 0 or x.data_ptr() % 16 != 0):
+        # no hidden copy: rows must start on 16-byte boundaries
+        raise ValueError(f"x rows must start on 16-byte boundaries (row stride {ldx} must be a multiple of 8, "
+                         "data 16-byte aligned); pass a [:, :K] view of a buffer with padded rows")
+    if M > 0 and x.untyped_storage().nbytes() - 2 * x.storage_offset() < 2 * M * ldx:
+        raise ValueError(f"x's storage must span M * row stride = {M * ldx} elements")
     ldq = ldq if ldq is not None else K + (-K) % 16
     dev = x.device
     xq = _out(out, (M, ldq), cd, dev, "out")
