@@ -37,6 +37,18 @@ int64_t w8a8_probe_sink_count(void);
  */
 w8a8_status w8a8_probe_mfma_i8(const void *a, const void *b, int64_t pairs, int32_t *sink, hipStream_t stream);
 
+/*
+ * The hardware e4m3 conversion the quantizers use, on consecutive f32 bit
+ * patterns: codes[i] = the OCP E4M3FN code (RNE) of the f32 value whose bit
+ * pattern is first_bits + i, after the quantizers' clamp to [-448, 448]
+ * (v_med3_f32, then v_cvt_pk_fp8_f32).  Lets a test compare the hardware
+ * encoding with a reference on every f32 of a range.
+ *   codes  device bytes [n].
+ * Errors: W8A8_ERR_INVALID_ARG (n < 0, null codes with n > 0, or
+ * first_bits + n > 2^32), W8A8_ERR_ALIGN; n == 0 is a no-op.
+ */
+w8a8_status w8a8_probe_cvt_e4m3(uint32_t first_bits, int64_t n, uint8_t *codes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,12 +18,17 @@ def test_exports_match_header():
     names = w8.exported_names_in_header()
     assert len(names) == 19
     probe = w8.exported_names_in_header(w8.PROBE_HEADER)
-    assert probe == ["w8a8_probe_mfma_i8", "w8a8_probe_sink_count"]
+    assert probe == ["w8a8_probe_cvt_e4m3", "w8a8_probe_mfma_i8", "w8a8_probe_sink_count"]
     for n in names + probe:
         assert hasattr(lib, n), n
 
 
 def test_probe_rejects():
+    assert lib.w8a8_probe_cvt_e4m3(0, -1, A, NULL) == INVALID
+    assert lib.w8a8_probe_cvt_e4m3(0, 4, NULL, NULL) == INVALID
+    assert lib.w8a8_probe_cvt_e4m3(0xFFFFFFF0, 17, A, NULL) == INVALID   # past 2^32 bit patterns
+    assert lib.w8a8_probe_cvt_e4m3(0, 4, MIS, NULL) == ALIGN
+    assert lib.w8a8_probe_cvt_e4m3(0, 0, A, NULL) == OK
     assert lib.w8a8_probe_mfma_i8(NULL, A, 1, A, NULL) == INVALID
     assert lib.w8a8_probe_mfma_i8(A, A, -1, A, NULL) == INVALID
     assert lib.w8a8_probe_mfma_i8(MIS, A, 1, A, NULL) == ALIGN

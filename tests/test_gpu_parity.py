@@ -917,3 +917,49 @@ def test_probe_mfma_runs():
     s2 = W8.probe_mfma_i8(r, r, 4)
     torch.cuda.synchronize()
     assert torch.equal(s1, s2) and s1.any()    # deterministic, not optimized away
+
+
+# ------------------------------------------------------------ e4m3 conversion
+def _oracle_e4m3_runs(sign_bit, last_bits):
+    """Start index (bit pattern offset from sign_bit) and oracle code of every
+    run of equal codes over the f32 bit patterns sign_bit + [0, last_bits]:
+    the oracle's encoding is monotone in the magnitude, so each code's run
+    starts at the smallest pattern that reaches it (binary search)."""
+    def code(offsets):
+        v = (np.asarray(offsets, np.uint64) + sign_bit).astype(np.uint32).view(np.float32)
+        return oracle.f32_to_e4m3(v).astype(np.int64) & 0x7F
+    top = int(code([last_bits])[0])
+    want = np.arange(1, top + 1)
+    lo = np.zeros(top, np.int64)
+    hi = np.full(top, last_bits, np.int64)
+    while (lo < hi).any():
+        mid = (lo + hi) // 2
+        ge = code(mid) >= want
+        hi = np.where(ge, mid, hi)
+        lo = np.where(ge, lo, mid + 1)
+    starts = np.concatenate([[0], lo])
+    codes = np.concatenate([[0], want]) | (0x80 if sign_bit else 0)
+    assert (oracle.f32_to_e4m3((starts.astype(np.uint64) + sign_bit).astype(np.uint32).view(np.float32)) ==
+            codes).all()
+    return starts, codes
+
+
+@pytest.mark.parametrize("sign_bit", [0, 0x80000000])
+def test_e4m3_conversion_every_f32_up_to_448(sign_bit):
+    """The hardware conversion the quantizers use (clamp to +-448, then
+    v_cvt_pk_fp8_f32) on every f32 bit pattern from +-0 to +-448 (1.14e9
+    values per sign), against the oracle's OCP E4M3FN encoding: the GPU codes
+    form runs, and every run must start at the oracle's boundary with the
+    oracle's code -- so each of the values gets the oracle's code."""
+    last = 0x43E00000                      # 448.0f
+    _say(f"e4m3 conversion of every f32 in sign {sign_bit:#x} [0, 448]")
+    starts, codes = _oracle_e4m3_runs(sign_bit, last)
+    got = W8.probe_cvt_e4m3(sign_bit, last + 1)
+    change = torch.nonzero(got[1:] != got[:-1]).flatten() + 1
+    g_starts = np.concatenate([[0], change.cpu().numpy()])
+    g_codes = got[torch.from_numpy(g_starts).cuda()].cpu().numpy()
+    torch.cuda.synchronize()
+    assert_equal(g_starts, starts, "run starts (bit-pattern offsets)")
+    assert_equal(g_codes, codes, "run codes")
+    del got, change
+    torch.cuda.empty_cache()

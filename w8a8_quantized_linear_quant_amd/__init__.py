@@ -17,6 +17,7 @@ the current stream.  The functions carry the C names:
   gguf_a8_requant_q8_0          Q8_0 weight -> int8 / e4m3 codes, one scale per output channel
   gguf_a8_linear                8-bit product with per-channel weight scales -> bf16
   probe_mfma_i8                 diagnostic: sustained int8 MFMA loop (include/w8a8_probe.h)
+  probe_cvt_e4m3                diagnostic: the hardware e4m3 conversion on consecutive f32 bit patterns
 
 Codes are torch.int8 (int8) or torch.float8_e4m3fn (e4m3); bf16 tensors are
 torch.bfloat16; scales are float32.  Output tensors may be passed in (`out=`)
@@ -72,6 +73,7 @@ def _load_library():
         "w8a8_hadamard_rotate": (I, [P, I64, I64, I64, P, I64, P]),
         "w8a8_probe_sink_count": (I64, []),
         "w8a8_probe_mfma_i8": (I, [P, P, I64, P, P]),
+        "w8a8_probe_cvt_e4m3": (I, [ctypes.c_uint32, I64, P, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -438,3 +440,12 @@ def probe_mfma_i8(a, b, pairs, sink=None):
     sink = _buf(sink, n, torch.int32, a.device, "sink")
     _check(_lib.w8a8_probe_mfma_i8(_ptr(a), _ptr(b), int(pairs), _ptr(sink), _stream(a.device)))
     return sink
+
+
+def probe_cvt_e4m3(first_bits, n, out=None, device=None):
+    """e4m3 codes (uint8 [n], on the GPU) of the f32 values with bit patterns
+    first_bits, first_bits + 1, ..., by the quantizers' clamp and conversion."""
+    dev = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    codes = _buf(out, n, torch.uint8, dev, "out", alloc=16)
+    _check(_lib.w8a8_probe_cvt_e4m3(ctypes.c_uint32(first_bits), n, _ptr(codes), _stream(dev)))
+    return codes[:n]
