@@ -63,7 +63,8 @@ typedef enum {
     W8A8_ERR_SHAPE = 2,       /* a size or stride that the layout rules below forbid */
     W8A8_ERR_ALIGN = 3,       /* a pointer that is not 16-byte aligned */
     W8A8_ERR_UNSUPPORTED = 4, /* a combination the library does not implement */
-    W8A8_ERR_HIP = 5          /* the HIP runtime reported a launch error */
+    W8A8_ERR_HIP = 5,         /* the HIP runtime reported a launch error */
+    W8A8_ERR_SCRATCH_LIMIT = 6 /* a call of svdq_linear_noalloc needs more than its fixed scratch */
 } w8a8_status;
 
 typedef enum {
@@ -197,6 +198,29 @@ w8a8_status svdq_linear(w8a8_qtype qtype, const uint16_t *x, int64_t M, int64_t 
                         const float *r_scale, const uint16_t *l1, const uint16_t *l2, int64_t r,
                         const uint16_t *bias, int64_t N, uint16_t *y, void *xq_out,
                         float *x_scale_out, void *workspace, hipStream_t stream);
+
+/*
+ * svdq_linear without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same launches and results as svdq_linear, with
+ * u kept in a fixed array of the library's own device memory,
+ * W8A8_SVDQ_NOALLOC_SCRATCH_BYTES (4 MiB) per GPU, held from the library's
+ * load on that GPU until the process ends.  Allocates nothing.
+ *   Arguments as svdq_linear, without workspace.
+ *   Limit: svdq_workspace_bytes(M, r) <= W8A8_SVDQ_NOALLOC_SCRATCH_BYTES,
+ *   i.e. M * roundup(r, 16) <= 2^20 (M <= 32768 at r = 32), else
+ *   W8A8_ERR_SCRATCH_LIMIT (checked before anything is launched).
+ *   `stream` must belong to the current device (else W8A8_ERR_INVALID_ARG).
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a
+ * GPU (different streams, or host threads) race and give undefined results;
+ * calls ordered on one stream are safe.  The array keeps the last call's u,
+ * which every call overwrites in full before reading it.
+ */
+#define W8A8_SVDQ_NOALLOC_SCRATCH_BYTES (4 * 1024 * 1024)
+w8a8_status svdq_linear_noalloc(w8a8_qtype qtype, const uint16_t *x, int64_t M, int64_t K, const void *rq,
+                                const float *r_scale, const uint16_t *l1, const uint16_t *l2, int64_t r,
+                                const uint16_t *bias, int64_t N, uint16_t *y, void *xq_out, float *x_scale_out,
+                                hipStream_t stream);
 
 /*
  * SVDQuant weight preparation (OneTrainer PR #1034 "SVDQuant"; wiki SVDQuant:

@@ -8,7 +8,7 @@ import pytest
 import w8a8_quantized_linear_quant_amd as w8
 
 lib = w8.library()
-OK, INVALID, SHAPE, ALIGN, UNSUPPORTED, HIPERR = range(6)
+OK, INVALID, SHAPE, ALIGN, UNSUPPORTED, HIPERR, SCRATCH_LIMIT = range(7)
 A = 1 << 20       # a 16-byte aligned fake address (never dereferenced)
 MIS = A + 1       # misaligned by one byte
 NULL = None
@@ -16,7 +16,7 @@ NULL = None
 
 def test_exports_match_header():
     names = w8.exported_names_in_header()
-    assert len(names) == 19
+    assert len(names) == 20
     probe = w8.exported_names_in_header(w8.PROBE_HEADER)
     assert probe == ["w8a8_probe_cvt_e4m3", "w8a8_probe_mfma_i8", "w8a8_probe_sink_count"]
     for n in names + probe:
@@ -36,7 +36,7 @@ def test_probe_rejects():
 
 
 def test_status_strings():
-    for code in range(6):
+    for code in range(7):
         assert lib.w8a8_status_str(code).decode().startswith("W8A8_")
     assert b"unknown" in lib.w8a8_status_str(99)
 
@@ -186,3 +186,23 @@ def test_hadamard_rejects():
     big = (1 << 30) + 16
     assert g(A, 4, big, big, A, big, NULL) == SHAPE                  # K > 2^30
     assert f(0, A, 4, big, big, A, big, A, NULL) == SHAPE
+
+
+def test_svdq_noalloc_scratch_limit():
+    """svdq_linear_noalloc rejects, before touching the device, a call whose
+    u (2 M roundup(r, 16) bf16) exceeds the fixed scratch; M = 0 is a no-op."""
+    import re
+    with open(w8.HEADER) as f:
+        m = re.search(r"#define W8A8_SVDQ_NOALLOC_SCRATCH_BYTES \((\d+) \* 1024 \* 1024\)", f.read())
+    assert m and int(m.group(1)) << 20 == w8.SVDQ_NOALLOC_SCRATCH_BYTES
+    f = lib.svdq_linear_noalloc
+    K, N, r = 64, 64, 32
+    over = w8.SVDQ_NOALLOC_SCRATCH_BYTES // (2 * 2 * 32) + 1            # one row too many at r = 32
+    assert w8.svdq_workspace_bytes(over, r) > w8.SVDQ_NOALLOC_SCRATCH_BYTES
+    assert f(0, A, over, K, A, A, A, A, r, NULL, N, A, A, A, NULL) == SCRATCH_LIMIT
+    assert f(0, A, 70000, K, A, A, A, A, 17, NULL, N, A, A, A, NULL) == SCRATCH_LIMIT  # rp = 32
+    assert f(0, A, 0, K, A, A, A, A, r, NULL, N, A, A, A, NULL) == OK
+    # the shared argument checks come first
+    assert f(0, A, 64, K, A, A, A, A, 65, NULL, N, A, A, A, NULL) == INVALID
+    assert f(0, A, 64, 40, A, A, A, A, r, NULL, N, A, A, A, NULL) == SHAPE
+    assert f(0, MIS, 64, K, A, A, A, A, r, NULL, N, A, A, A, NULL) == ALIGN

@@ -12,6 +12,7 @@ the current stream.  The functions carry the C names:
   w8a8_linear_backward_dx       dX = dY . W from quantized dY and W^T codes
   w8a8_gemm_i32                 raw int32 accumulators (test export)
   svdq_linear                   residual 8-bit product + bf16 low-rank branch
+  svdq_linear_noalloc           the same with its workspace in a fixed per-GPU scratch (allocates nothing)
   svdq_prepare                  W -> bf16 low-rank pair (truncated SVD) + bf16 residual
   q8_0_quantize / q8_0_dequantize / q8_0_nbytes   GGUF Q8_0 blocks
   gguf_a8_requant_q8_0          Q8_0 weight -> int8 / e4m3 codes, one scale per output channel
@@ -61,6 +62,7 @@ def _load_library():
         "w8a8_gemm_i32": (I, [P, P, I64, I64, I64, P, P]),
         "svdq_workspace_bytes": (ctypes.c_size_t, [I64, I64]),
         "svdq_linear": (I, [I, P, I64, I64, P, P, P, P, I64, P, I64, P, P, P, P, P]),
+        "svdq_linear_noalloc": (I, [I, P, I64, I64, P, P, P, P, I64, P, I64, P, P, P, P]),
         "q8_0_nbytes": (ctypes.c_size_t, [I64]),
         "q8_0_quantize": (I, [P, I64, P, P]),
         "q8_0_dequantize": (I, [P, I64, P, P]),
@@ -90,6 +92,7 @@ def exported_names_in_header(path=HEADER):
     with open(path) as f:
         text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"^\s*#.*$", "", text, flags=re.M)   # preprocessor lines
     return sorted(set(re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*\(", text)) -
                   {"if", "defined", "sizeof", "extern"})
 
@@ -321,9 +324,7 @@ def svdq_workspace_bytes(M, r):
     return int(_lib.svdq_workspace_bytes(M, r))
 
 
-def svdq_linear(x, rq, r_scale, l1, l2, bias=None, out=None, xq_out=None, x_scale_out=None, workspace=None):
-    """x bf16 [M, K]; rq residual codes [N, K]; l1 bf16 [r, K]; l2 bf16 [N, r].
-    Returns (y bf16 [M, N], xq [M, K], x_scale [M])."""
+def _svdq_args(x, rq, r_scale, l1, l2, bias, out, xq_out, x_scale_out):
     qt = _qtype_of(rq)
     _need(x, torch.bfloat16, "x")
     dev = x.device
@@ -344,10 +345,32 @@ def svdq_linear(x, rq, r_scale, l1, l2, bias=None, out=None, xq_out=None, x_scal
     y = _out(out, (M, N), torch.bfloat16, dev, "out")
     xq = _out(xq_out, (M, K), rq.dtype, dev, "xq_out")
     sx = _buf(x_scale_out, M, torch.float32, dev, "x_scale_out")
+    return qt, dev, x, rq, r_scale, l1, l2, bias, M, N, K, r, y, xq, sx
+
+
+def svdq_linear(x, rq, r_scale, l1, l2, bias=None, out=None, xq_out=None, x_scale_out=None, workspace=None):
+    """x bf16 [M, K]; rq residual codes [N, K]; l1 bf16 [r, K]; l2 bf16 [N, r].
+    Returns (y bf16 [M, N], xq [M, K], x_scale [M])."""
+    qt, dev, x, rq, r_scale, l1, l2, bias, M, N, K, r, y, xq, sx = _svdq_args(x, rq, r_scale, l1, l2, bias, out,
+                                                                             xq_out, x_scale_out)
     ws = _buf(workspace, svdq_workspace_bytes(M, r), torch.uint8, dev, "workspace", alloc=16)
     _check(_lib.svdq_linear(qt, _ptr(x), M, K, _ptr(rq), _ptr(r_scale), _ptr(l1), _ptr(l2), r, _ptr(bias), N,
                             _ptr(y), _ptr(xq), _ptr(sx), _ptr(ws), _stream(dev)))
     return y, xq, sx[:M]
+
+
+def svdq_linear_noalloc(x, rq, r_scale, l1, l2, bias=None, out=None, xq_out=None, x_scale_out=None):
+    """svdq_linear with its workspace in the library's fixed per-GPU scratch
+    (W8A8_SVDQ_NOALLOC_SCRATCH_BYTES): the C call allocates nothing.  Pass
+    `out`, `xq_out` and `x_scale_out` to allocate nothing here either."""
+    qt, dev, x, rq, r_scale, l1, l2, bias, M, N, K, r, y, xq, sx = _svdq_args(x, rq, r_scale, l1, l2, bias, out,
+                                                                             xq_out, x_scale_out)
+    _check(_lib.svdq_linear_noalloc(qt, _ptr(x), M, K, _ptr(rq), _ptr(r_scale), _ptr(l1), _ptr(l2), r, _ptr(bias),
+                                    N, _ptr(y), _ptr(xq), _ptr(sx), _stream(dev)))
+    return y, xq, sx[:M]
+
+
+SVDQ_NOALLOC_SCRATCH_BYTES = 4 * 1024 * 1024
 
 
 def svdq_prepare_subspace(r):

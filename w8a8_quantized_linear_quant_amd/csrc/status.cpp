@@ -9,6 +9,8 @@ extern "C" const char *w8a8_status_str(w8a8_status status) {
     case W8A8_ERR_ALIGN: return "W8A8_ERR_ALIGN: pointer not 16-byte aligned";
     case W8A8_ERR_UNSUPPORTED: return "W8A8_ERR_UNSUPPORTED: combination not implemented";
     case W8A8_ERR_HIP: return "W8A8_ERR_HIP: the HIP runtime reported a launch error";
+    case W8A8_ERR_SCRATCH_LIMIT:
+        return "W8A8_ERR_SCRATCH_LIMIT: the call needs more than the no-alloc entry point's fixed scratch";
     }
     return "unknown w8a8_status";
 }

@@ -13,6 +13,8 @@
 // the up-projection does not round u to 8 bits); (3) the 8-bit product whose
 // epilogue adds hi . L2^T + lo . L2^T with the bf16 MFMA before the bias.
 // For K <= 4096 and r <= 32, (1) and (2) are one kernel reading X once.
+#include <atomic>
+
 #include "act_quant.hpp"
 
 namespace w8a8 {
@@ -200,19 +202,29 @@ extern "C" size_t svdq_workspace_bytes(int64_t M, int64_t r) {
     return (size_t)(2 * M * w8a8::round_up16(r) * sizeof(uint16_t));
 }
 
-extern "C" w8a8_status svdq_linear(w8a8_qtype qtype, const uint16_t *x, int64_t M, int64_t K, const void *rq,
-                                   const float *r_scale, const uint16_t *l1, const uint16_t *l2, int64_t r,
-                                   const uint16_t *bias, int64_t N, uint16_t *y, void *xq_out, float *x_scale_out,
-                                   void *workspace, hipStream_t stream) {
-    using namespace w8a8;
+namespace w8a8 {
+namespace {
+
+// Argument checks shared by svdq_linear and svdq_linear_noalloc (the
+// workspace is checked by the caller).
+w8a8_status svdq_check(w8a8_qtype qtype, const uint16_t *x, int64_t M, int64_t K, const void *rq,
+                       const float *r_scale, const uint16_t *l1, const uint16_t *l2, int64_t r, const uint16_t *bias,
+                       int64_t N, const uint16_t *y, const void *xq_out, const float *x_scale_out) {
     if (!valid_qtype(qtype) || r < 1 || r > kMaxRp) return W8A8_ERR_INVALID_ARG;
     w8a8_status st = gemm_check(xq_out, rq, M, N, K, y);
     if (st != W8A8_OK) return st;
     st = act_quant_check(qtype, x, M, K, K, xq_out, K, x_scale_out);
     if (st != W8A8_OK) return st;
-    if (M > 0 && N > 0 && (!r_scale || !l1 || !l2 || !workspace)) return W8A8_ERR_INVALID_ARG;
-    if (!aligned16(r_scale) || !aligned16(l1) || !aligned16(l2) || !aligned16(bias) || !aligned16(workspace))
-        return W8A8_ERR_ALIGN;
+    if (M > 0 && N > 0 && (!r_scale || !l1 || !l2)) return W8A8_ERR_INVALID_ARG;
+    if (!aligned16(r_scale) || !aligned16(l1) || !aligned16(l2) || !aligned16(bias)) return W8A8_ERR_ALIGN;
+    return W8A8_OK;
+}
+
+// The launches, on checked arguments; `workspace` holds u (hi, then lo).
+w8a8_status svdq_run(w8a8_qtype qtype, const uint16_t *x, int64_t M, int64_t K, const void *rq, const float *r_scale,
+                     const uint16_t *l1, const uint16_t *l2, int64_t r, const uint16_t *bias, int64_t N, uint16_t *y,
+                     void *xq_out, float *x_scale_out, void *workspace, hipStream_t stream) {
+    w8a8_status st = W8A8_OK;
     if (M == 0) return W8A8_OK;
     const int rp = (int)round_up16(r);
     uint16_t *uhi = static_cast<uint16_t *>(workspace);
@@ -255,4 +267,70 @@ extern "C" w8a8_status svdq_linear(w8a8_qtype qtype, const uint16_t *x, int64_t 
     // r of 16 or 32: the low-rank operands are staged in LDS (r == rp keeps
     // the staged l2 rows aligned); other ranks read them from global memory
     return gemm_launch(qtype, (r == 16 || r == 32) ? kEpiLowRank32 : kEpiLowRank, a, stream);
+}
+
+}  // namespace
+}  // namespace w8a8
+
+extern "C" w8a8_status svdq_linear(w8a8_qtype qtype, const uint16_t *x, int64_t M, int64_t K, const void *rq,
+                                   const float *r_scale, const uint16_t *l1, const uint16_t *l2, int64_t r,
+                                   const uint16_t *bias, int64_t N, uint16_t *y, void *xq_out, float *x_scale_out,
+                                   void *workspace, hipStream_t stream) {
+    using namespace w8a8;
+    w8a8_status st = svdq_check(qtype, x, M, K, rq, r_scale, l1, l2, r, bias, N, y, xq_out, x_scale_out);
+    if (st != W8A8_OK) return st;
+    if (M > 0 && N > 0 && !workspace) return W8A8_ERR_INVALID_ARG;
+    if (!aligned16(workspace)) return W8A8_ERR_ALIGN;
+    return svdq_run(qtype, x, M, K, rq, r_scale, l1, l2, r, bias, N, y, xq_out, x_scale_out, workspace, stream);
+}
+
+// ------------------------------------------------------------------------
+// svdq_linear_noalloc: the same launches with u in a fixed device array of
+// the library instead of a caller workspace, for callers that cannot
+// allocate.  Each GPU holds its own copy of the array from the time the
+// library's code object is loaded on it until the process ends.  u is
+// written in full (every row < M, every column < rp) before it is read, so
+// the contents a previous call left there never reach a result and nothing
+// is cleared.  Calls that overlap on one GPU (different streams, or host
+// threads) share the array and race.
+static __device__ __align__(256) uint8_t scratch[W8A8_SVDQ_NOALLOC_SCRATCH_BYTES];
+
+namespace w8a8 {
+namespace {
+
+// Device address of `scratch` on device `dev` (the current device), taken
+// once per device: the name of the array in host code is a host-side
+// stand-in, not a device address.  Threads racing on the first query store
+// the same value.
+void *scratch_address(int dev) {
+    static std::atomic<void *> cached[64] = {};
+    if (dev < 0 || dev >= 64) return nullptr;
+    void *ptr = cached[dev].load(std::memory_order_acquire);
+    if (ptr) return ptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    cached[dev].store(ptr, std::memory_order_release);
+    return ptr;
+}
+
+}  // namespace
+}  // namespace w8a8
+
+extern "C" w8a8_status svdq_linear_noalloc(w8a8_qtype qtype, const uint16_t *x, int64_t M, int64_t K,
+                                           const void *rq, const float *r_scale, const uint16_t *l1,
+                                           const uint16_t *l2, int64_t r, const uint16_t *bias, int64_t N,
+                                           uint16_t *y, void *xq_out, float *x_scale_out, hipStream_t stream) {
+    using namespace w8a8;
+    w8a8_status st = svdq_check(qtype, x, M, K, rq, r_scale, l1, l2, r, bias, N, y, xq_out, x_scale_out);
+    if (st != W8A8_OK) return st;
+    if (svdq_workspace_bytes(M, r) > (size_t)W8A8_SVDQ_NOALLOC_SCRATCH_BYTES) return W8A8_ERR_SCRATCH_LIMIT;
+    if (M == 0) return W8A8_OK;
+    // the scratch of the device the stream runs on, which must be current
+    int dev = -1, sdev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return W8A8_ERR_HIP;
+    if (stream == nullptr) sdev = dev;  // the null stream is the current device's
+    else if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return W8A8_ERR_HIP;
+    if (dev != sdev) return W8A8_ERR_INVALID_ARG;
+    void *ws = scratch_address(dev);
+    if (!ws) return W8A8_ERR_HIP;
+    return svdq_run(qtype, x, M, K, rq, r_scale, l1, l2, r, bias, N, y, xq_out, x_scale_out, ws, stream);
 }
