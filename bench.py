@@ -44,8 +44,13 @@ def _args():
     p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-rows", action="store_true", help="skip the per-row figures of the other paths")
-    p.add_argument("--cpu-rows", type=int, default=1024,
-                   help="rows of the oracle sample (about 15 s of one CPU core)")
+    p.add_argument("--cpu-rows", type=int, default=512,
+                   help="rows of the one-thread oracle sample (about 7 s of one CPU core)")
+    p.add_argument("--cpu-rows-all", type=int, default=M,
+                   help="rows of the all-thread oracle sample")
+    p.add_argument("--settle-ms", type=float, default=100.0,
+                   help="untimed steps for at least this long before the warm-up steps (the GPU's clock ramps "
+                        "under a sustained load for ~30 ms)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="also run one plain 512 MiB device copy (reference for HBM byte counters)")
     return p.parse_args()
@@ -124,22 +129,56 @@ def measured_peaks(w8, torch, a_codes, b_codes):
     return round(mfma_tops, 1), round(copy_gbs, 1)
 
 
-def cpu_baseline(x_bits, w_bits, b_bits, rows):
-    """The oracle (plain C, one thread) on the first `rows` rows of the same
-    workload: act-quant + weight quant + linear, scaled to TOPS of the linear."""
+def cpu_baseline(x_bits, w_bits, b_bits, rows, rows_all):
+    """The oracle (plain C) on the same workload, scaled to TOPS of the linear:
+    act-quant + int8 linear of the first `rows` rows on one thread, then of
+    the first `rows_all` rows split into row slices over all host threads
+    (a thread pool calling the oracle's C functions, which release the GIL;
+    the oracle's arithmetic is untouched).  The weight quantization is timed
+    apart (once per frozen weight)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
-    xs = x_bits[:rows]
     t0 = time.perf_counter()
     wq, _, sw = oracle.quant_weight_tensorwise(oracle.INT8, w_bits)
     t1 = time.perf_counter()
-    xq, sx = oracle.quant_act_rowwise(oracle.INT8, xs)
-    oracle.linear(oracle.INT8, xq, sx, wq, sw, b_bits)
+
+    def run(lo, hi):
+        xq, sx = oracle.quant_act_rowwise(oracle.INT8, x_bits[lo:hi])
+        oracle.linear(oracle.INT8, xq, sx, wq, sw, b_bits)
+
+    run(0, rows)
     t2 = time.perf_counter()
-    ops = 2.0 * rows * N * K
-    return {"value": round(ops / (t2 - t1) / 1e12, 6), "unit": "TOPS", "cores": 1, "kind": "oracle",
-            "sample": f"first {rows} of {M} rows: act-quant + int8 linear ({rows}x{N}x{K}); "
-                      f"weight quant ({N}x{K}) timed apart: {t1 - t0:.2f} s",
-            "seconds": round(t2 - t1, 2), "host_cpu": _host_cpu(), "host_threads": os.cpu_count()}
+    threads = _host_threads()
+    step = -(-rows_all // threads)
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        t3 = time.perf_counter()
+        list(ex.map(lambda i: run(i, min(i + step, rows_all)), range(0, rows_all, step)))
+        t4 = time.perf_counter()
+    one = 2.0 * rows * N * K / (t2 - t1) / 1e12
+    allc = 2.0 * rows_all * N * K / (t4 - t3) / 1e12
+    return {"value": round(allc, 6), "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"act-quant + int8 linear of the first {rows_all} of {M} rows ({rows_all}x{N}x{K}) in "
+                      f"{threads} row slices on {threads} threads; weight quant ({N}x{K}, one thread) timed "
+                      f"apart: {t1 - t0:.2f} s",
+            "seconds": round(t4 - t3, 2),
+            "single_thread": {"value": round(one, 6), "unit": "TOPS", "cores": 1, "seconds": round(t2 - t1, 2),
+                              "sample": f"first {rows} rows ({rows}x{N}x{K})"},
+            "host_cpu": _host_cpu(), "host_threads": os.cpu_count()}
+
+
+def _host_threads():
+    """Threads the CPU baseline may use: the process's CPU affinity, else
+    os.cpu_count(), capped by OMP_NUM_THREADS where that is set (the host
+    share the process was given)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
 
 
 def _host_cpu():
@@ -195,7 +234,21 @@ def main():
         act_quant(i)
         gemm(i)
 
-    # ---- the timed steps
+    # ---- the timed steps.  The GPU's clock ramps for ~30 ms under a sustained
+    # load and again after an idle pause: steps run untimed until settle_ms
+    # of them have passed, then the W warm-up steps, then the K timed ones.
+    settle_steps = 0
+    if args.settle_ms > 0:
+        es0, es1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        es0.record()
+        while True:
+            for _ in range(10):
+                step(settle_steps)
+                settle_steps += 1
+            es1.record()
+            es1.synchronize()
+            if es0.elapsed_time(es1) >= args.settle_ms:
+                break
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -235,6 +288,8 @@ def main():
     khash = _kernel_hash()
     roofline = {"bound": "mfma", "achieved": round(gemm_tops, 1), "peak": PEAK_INT8_TOPS, "unit": "TOPS",
                 "frac": round(gemm_tops / PEAK_INT8_TOPS, 4), "traffic": _traffic_from_profile(khash),
+                "traffic_counts": "L2-to-fabric bytes per launch (FETCH_SIZE + WRITE_SIZE): L2 misses, "
+                                  "including those the Infinity Cache serves, not HBM bytes alone",
                 "kernel": "gemm_kernel<int8, bf16 epilogue>", "us_per_launch": round(ms_gemm * 1e3, 2),
                 "algorithmic_ops_per_launch": ops, "kernel_source_hash": khash, **spread}
     act = {"bound": "hbm", "achieved": round(aq_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -244,7 +299,7 @@ def main():
     # the same rates against ceilings measured here, in the same power state
     mfma_tops, copy_gbs = measured_peaks(w8, torch, sets[0]["xq"], sets[0]["wq"])
     roofline.update(measured_peak=mfma_tops, frac_of_measured_peak=round(gemm_tops / mfma_tops, 4),
-                    measured_peak_how="int8 MFMA loop (v_mfma_i32_32x32x32_i8, one wave per SIMD, all CUs) "
+                    measured_peak_how="int8 MFMA loop (v_mfma_i32_16x16x64_i8, the GEMM's instruction, one wave per SIMD, all CUs) "
                                       "on fragments of this step's activation and weight codes")
     act.update(measured_peak=copy_gbs, frac_of_measured_peak=round(aq_gbs / copy_gbs, 4),
                measured_peak_how="device-to-device copy of 512 MiB, read + write bytes")
@@ -265,7 +320,7 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(x_bits, r_bits, b_bits, args.cpu_rows)
+        cpu = cpu_baseline(x_bits, r_bits, b_bits, args.cpu_rows, args.cpu_rows_all)
 
     out = {
         "metric": "W8A8 linear TOPS (M4096 K3072 N12288) + act-quant GB/s, % of roofline",
@@ -274,7 +329,8 @@ def main():
         "dtype": "int8", "data": "synthetic (seeded numpy PCG64, transformer-shaped; no dataset)",
         "config": {"workload": "int W8A8 linear forward: row-wise act-quant X[4096,3072] bf16 + int8 GEMM "
                                "vs W[12288,3072] (tensor-wise) + dequant/bias epilogue -> bf16 Y",
-                   "M": M, "K": K, "N": N, "bias": True, "rotating_buffer_sets": ROTATE},
+                   "M": M, "K": K, "N": N, "bias": True, "rotating_buffer_sets": ROTATE,
+                   "settle_steps": settle_steps, "settle_ms": args.settle_ms},
         "roofline": roofline,
         "act_quant": act,
         "cpu_baseline": cpu,
@@ -344,11 +400,24 @@ def other_rows(w8, torch, workloads, args):
         y = torch.empty((4608, nn), dtype=torch.bfloat16, device="cuda")
         ms = _time_row(lambda i: w8.w8a8_linear(xq, sx, wq, sw, bb, out=y))
         res[name] = {"us": round(ms * 1e3, 1), "TOPS": round(2.0 * 4608 * nn * 3072 / ms / 1e9, 1)}
-    del x, xq, y
+    # act-quant of the DiT X [4608, 3072] (int8), 16 cold buffer sets
+    aq = [(x if j == 0 else x.clone(), torch.empty((4608, K), dtype=torch.int8, device="cuda"),
+           torch.empty(4608, dtype=torch.float32, device="cuda")) for j in range(AQ_ROTATE)]
+    ms = _time_row(lambda i: w8.w8a8_quant_act_rowwise(aq[i % AQ_ROTATE][0], out=aq[i % AQ_ROTATE][1],
+                                                       scale=aq[i % AQ_ROTATE][2]))
+    res["act_quant_int8_X4608x3072"] = {"us": round(ms * 1e3, 1), "GB/s": round((3.0 * 4608 * K + 4 * 4608) / ms / 1e6, 1)}
+    del x, xq, y, aq
     # fp8 train step shapes
     d = workloads.fp8_step()
     wq, wqt, sw = w8.w8a8_quant_weight_tensorwise(_bf16(d["w"]), qtype=w8.FP8_E4M3, transposed=True)
     x = _bf16(d["x"])
+    # act-quant of the forward X [8192, 3072] (e4m3), 8 cold buffer sets of 75.5 MB
+    aq = [(x if j == 0 else x.clone(), torch.empty((8192, K), dtype=torch.float8_e4m3fn, device="cuda"),
+           torch.empty(8192, dtype=torch.float32, device="cuda")) for j in range(8)]
+    ms = _time_row(lambda i: w8.w8a8_quant_act_rowwise(aq[i % 8][0], qtype=w8.FP8_E4M3, out=aq[i % 8][1],
+                                                       scale=aq[i % 8][2]))
+    res["act_quant_fp8_X8192x3072"] = {"us": round(ms * 1e3, 1), "GB/s": round((3.0 * 8192 * K + 4 * 8192) / ms / 1e6, 1)}
+    del aq
     xq, sx = w8.w8a8_quant_act_rowwise(x, qtype=w8.FP8_E4M3)
     y = torch.empty((8192, N), dtype=torch.bfloat16, device="cuda")
     ms = _time_row(lambda i: w8.w8a8_linear(xq, sx, wq, sw, out=y))
@@ -371,16 +440,20 @@ def other_rows(w8, torch, workloads, args):
     res["int8_bwd_dx_M8192_N12288_K3072"] = {"us": round(ms * 1e3, 1),
                                              "TOPS": round(2.0 * 8192 * N * K / ms / 1e9, 1)}
     del wq, wqt, x, xq, y, dy, dyq, dx, wq8, wqt8, dyq8
-    # Q8_0 (4 buffer sets of 85 MB: every launch reads cold HBM, not the 256 MB Infinity Cache)
+    # Q8_0 (8 buffer sets of 85 MB, 680 MB in all: every launch reads cold HBM,
+    # not the 256 MB Infinity Cache)
     v0 = torch.from_numpy(workloads.q8_0_vector()).cuda()
     n = v0.numel()
     qs = [(v0 if j == 0 else v0.clone(), torch.empty(w8.q8_0_nbytes(n), dtype=torch.uint8, device="cuda"),
-           torch.empty(n, dtype=torch.float32, device="cuda")) for j in range(4)]
-    ms = _time_row(lambda i: w8.q8_0_quantize(qs[i % 4][0], out=qs[i % 4][1]))
+           torch.empty(n, dtype=torch.float32, device="cuda")) for j in range(8)]
+    ms = _time_row(lambda i: w8.q8_0_quantize(qs[i % 8][0], out=qs[i % 8][1]))
     qbytes = 4.0 * n + w8.q8_0_nbytes(n)
     res["q8_0_quantize_n16777221"] = {"us": round(ms * 1e3, 1), "GB/s": round(qbytes / ms / 1e6, 1)}
-    ms = _time_row(lambda i: w8.q8_0_dequantize(qs[i % 4][1], n, out=qs[i % 4][2]))
-    res["q8_0_dequantize_n16777221"] = {"us": round(ms * 1e3, 1), "GB/s": round(qbytes / ms / 1e6, 1)}
+    ms = _time_row(lambda i: w8.q8_0_dequantize(qs[i % 8][1], n, out=qs[i % 8][2]))
+    res["q8_0_dequantize_n16777221"] = {
+        "us": round(ms * 1e3, 1), "GB/s": round(qbytes / ms / 1e6, 1),
+        "note": "reads are cold; its 67 MB of f32 output per launch is written back from the Infinity Cache "
+                "(write-back) partly after the launch, so the rate is not a cold-HBM write rate"}
     del v0, qs
     # GGUF A8: Q8_0 weight [12288, 3072] -> per-channel int8 / e4m3, then the linear at the headline shape
     d = workloads.gguf()

@@ -24,11 +24,11 @@ int64_t w8a8_probe_sink_count(void);
 
 /*
  * Sustained int8 MFMA rate on given operand bytes: one workgroup of 4 waves
- * per compute unit, each wave looping `pairs` times over 32 products
- * v_mfma_i32_32x32x32_i8 (two alternating sets of 4 x 4 fragments read once
- * from the first 64 KiB of a and of b) into 16 independent 32x32
- * accumulators.  Integer operations per call:
- *   pairs * 32 * 2 * 32 * 32 * 32 * 4 * (compute units).
+ * per compute unit, each wave looping `pairs` times over 64 products
+ * v_mfma_i32_16x16x64_i8 (8 x 8 fragments read once from the first 64 KiB of
+ * a and of b) into 64 independent 16x16 accumulators.  Integer operations
+ * per call: pairs * 64 * 2 * 16 * 16 * 64 * 4 * (compute units), which equals
+ * pairs * 32 * 2 * 32 * 32 * 32 * 4 * (compute units).
  *   a, b   device bytes, at least 65536 each (e.g. activation and weight codes,
  *          so that the matrix cores see the workload's value distribution).
  *   sink   int32 [w8a8_probe_sink_count()]: an xor of each lane's results.

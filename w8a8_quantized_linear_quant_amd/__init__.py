@@ -452,9 +452,9 @@ def gguf_a8_linear(xq, x_scale, wq, w_scale, bias=None, out=None):
 # ---------------------------------------------------------------- diagnostics
 def probe_mfma_i8(a, b, pairs, sink=None):
     """Sustained int8 MFMA loop on operand bytes `a`, `b` (device tensors of at
-    least 65536 bytes each): `pairs` iterations of 32 products per wave, one
-    workgroup of 4 waves per CU.  Returns the sink tensor; the integer
-    operations are pairs * 32 * 2 * 32**3 * 4 * CUs."""
+    least 65536 bytes each): `pairs` iterations of 64 v_mfma_i32_16x16x64_i8
+    per wave, one workgroup of 4 waves per CU.  Returns the sink tensor; the
+    integer operations are pairs * 32 * 2 * 32**3 * 4 * CUs."""
     import torch
     for t in (a, b):
         if t.numel() * t.element_size() < 65536 or not t.is_contiguous():

@@ -70,6 +70,14 @@ static_assert((NST - 1) * kLoadsPerStage <= 63, "vmcnt range");
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// in 6:4, lgkmcnt in 11:8; a field at its maximum does not wait).  Issued
+// with __builtin_amdgcn_s_waitcnt, unlike inline asm, they enter the
+// compiler's model of the outstanding counters, so it adds no waits of its
+// own for what they already cover.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+
 // XOR swizzle of the 16-byte chunk index by row, chosen so that the fragment
 // reads of 16 consecutive rows (same logical chunk) spread over distinct bank
 // groups whether the LDS serves 8 or 16 lanes of a 128-bit read per cycle.
@@ -77,6 +85,33 @@ typedef __attribute__((address_space(3))) void *lds_ptr_t;
 __device__ __forceinline__ int swz(int row) {
     if constexpr (kChunks == 8) return (row & 7) ^ ((row >> 3) & 1);
     else return ((row >> 1) ^ (row >> 2)) & 3;
+}
+
+// Placement of the int8 stage's memory instructions among its 16 groups of
+// 4 MFMAs: after group g, fragment reads i8_read_first(g) ..
+// + i8_reads_after(g) - 1 of the next stage, and one refill load (part
+// i8_load_part(g) of the stage's loads) if i8_loads_after(g).
+#ifndef W8A8_GEMM_I8_SCHED
+#define W8A8_GEMM_I8_SCHED 2
+#endif
+constexpr int i8_reads_after(int g) {
+    if (W8A8_GEMM_I8_SCHED == 0) return g < 8 ? 2 : 0;    // reads in the first half
+    if (W8A8_GEMM_I8_SCHED == 1) return g == 0 ? 16 : 0;  // reads together after the first group
+    return 1;                                             // one read per group (2, 3)
+}
+constexpr int i8_read_first(int g) {
+    int n = 0;
+    for (int i = 0; i < g; ++i) n += i8_reads_after(i);
+    return n;
+}
+constexpr bool i8_loads_after(int g) {
+    if (W8A8_GEMM_I8_SCHED == 2) return g % 2 == 1;      // one load per two groups
+    return g >= 8;                                        // loads in the second half (0, 1, 3)
+}
+constexpr int i8_load_part(int g) {
+    int n = 0;
+    for (int i = 0; i < g; ++i) n += i8_loads_after(i) ? 1 : 0;
+    return n;
 }
 
 struct TileCoord {
@@ -128,6 +163,33 @@ __device__ __forceinline__ v16f low_rank_add(const GemmArgs &p, v16f v, int nbas
     return v;
 }
 
+
+// The same for a 16x16 block (16x16x32 bf16 MFMA; lane l holds l2 row
+// nbase + (l & 15) and u row mbase + (l & 15), rank columns 8 (l >> 4) + 0..7
+// of each 32-column step; C layout as the int8 product).
+__device__ __forceinline__ v4f low_rank_add16(const GemmArgs &p, v4f v, int nbase, int mbase, int brow, int lane) {
+    const int nrow = nbase + brow, m = mbase + brow;
+    const int jq = (lane >> 4) * 8;
+    for (int ks = 0; ks < p.rp; ks += 32) {
+        const int j0 = ks + jq;
+        uint16_t ta[8];
+        if (nrow < p.N && (p.r & 7) == 0 && j0 + 8 <= p.r) {
+            *reinterpret_cast<v4u *>(ta) = *reinterpret_cast<const v4u *>(p.l2 + (size_t)nrow * p.r + j0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ta[i] = (nrow < p.N && j0 + i < p.r) ? p.l2[(size_t)nrow * p.r + j0 + i] : 0;
+        }
+        const v8bf a = __builtin_bit_cast(v8bf, ta);
+        v4u zh = {0u, 0u, 0u, 0u}, zl = {0u, 0u, 0u, 0u};
+        if (m < p.M && j0 < p.rp) {
+            zh = *reinterpret_cast<const v4u *>(p.uhi + (size_t)m * p.rp + j0);
+            zl = *reinterpret_cast<const v4u *>(p.ulo + (size_t)m * p.rp + j0);
+        }
+        v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, zh), v, 0, 0, 0);
+        v = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf, zl), v, 0, 0, 0);
+    }
+    return v;
+}
 
 // TAIL: K is not a multiple of BK * NST, so some stages reach past K and
 // need per-lane range checks; otherwise every stage is whole and the stage's
@@ -239,38 +301,51 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         }
     };
 
-    // MFMA fragments: lane row = l & 31 within a 32-row block (swz(row)
-    // depends on l & 15 only); int8 takes 16 bytes per lane per k-step of 32,
-    // e4m3 32 bytes per k-step of 64.
+    // MFMA shapes.  int8: v_mfma_i32_16x16x64_i8, the wave's 128x128 as 8x8
+    // blocks of 16x16 (4 accumulators per lane each).  It does the work of
+    // the 32x32x32 form with half the accumulator traffic per product (4
+    // accumulators read and written per 16K products instead of 16 per 32K),
+    // and sustains ~22% more int8
+    // operations per second than it on this chip under its power limit
+    // (measured with both in a pure MFMA loop on the workload's codes).
+    // e4m3: v_mfma_scale_f32_32x32x64_f8f6f4, 4x4 blocks of 32x32 (16 each).
+    // Both take 64 bytes of K per lane row and instruction: one k-step per
+    // 64-byte stage.
     constexpr bool kInt8 = QT == W8A8_INT8;
-    constexpr int KSTEPS = kInt8 ? BK / 32 : BK / 64;
+    constexpr int kBlk = kInt8 ? 16 : 32;  // edge of one MFMA output block
+    constexpr int kNB = 128 / kBlk;        // blocks along each edge of the wave tile
+    constexpr int kQuads = kBlk * kBlk / 64 / 4;  // groups of 4 consecutive columns per lane and block
+    constexpr int KSTEPS = BK / 64;
     static_assert(KSTEPS >= 1, "stage too small for one MFMA k-step");
+    static_assert(!kInt8 || BK == 64, "int8 fragment offsets assume one k-step of 64 bytes per stage");
     typedef typename std::conditional<kInt8, v4i, v8i>::type frag_t;
-    typedef typename std::conditional<kInt8, v16i, v16f>::type acc_t;
+    typedef typename std::conditional<kInt8, v4i, v16f>::type acc_t;  // one block's accumulators
+    typedef acc_t blk_t;
     const int lrow = lane & 31, half = lane >> 5;
     const int lsw = swz(lrow);
 
-    acc_t acc[4][4];
-    frag_t fa[2][4], fb[2][4];
+    acc_t acc[kNB][kNB];
+    auto blk = [&](int nb, int mb) -> blk_t { return acc[nb][mb]; };
+    auto set_blk = [&](int nb, int mb, blk_t c) { acc[nb][mb] = c; };
+    frag_t fa[2][kNB], fb[2][kNB];
 
-    // int8: lane offsets of the fragment reads of k-steps 0 and 1 of a stage.
-    // Each read_frags call adds one to its stage's base through an opaque
-    // copy, so the compiler does not keep a precomputed address per stage
-    // buffer and k-step alive across the loop (measured: ~3% faster for int8;
-    // e4m3, with half as many k-steps, is faster with the addresses kept).
-    int foff[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) foff[kk] = lrow * BK + (((kk * 2 + half) ^ lsw) << 4);
+    // int8: lane l reads row l & 15 of each 16-row block, 16-byte chunk
+    // l >> 4 (the chunk XOR-swizzled by the row).  read_frags adds the lane
+    // offset to the stage's base through an opaque copy, so the compiler
+    // does not keep a precomputed address per stage buffer alive across the
+    // loop.
+    const int foff = (lane & 15) * BK + (((lane >> 4) ^ swz(lane & 15)) << 4);
     auto read_frags = [&](const uint8_t *stage, int kk, frag_t *af, frag_t *bf) {
         const uint8_t *xs = stage + (wm * 128) * BK;            // X rows of this wave
         const uint8_t *ws = stage + kOpBytes + (wn * 128) * BK;  // W rows of this wave
         if constexpr (kInt8) {
-            int off = foff[kk & 1];
+            (void)kk;
+            int off = foff;
             asm volatile("" : "+v"(off));
 #pragma unroll
-            for (int b = 0; b < 4; ++b) af[b] = *reinterpret_cast<const v4i *>(ws + b * 32 * BK + off);
+            for (int b = 0; b < kNB; ++b) af[b] = *reinterpret_cast<const v4i *>(ws + b * 16 * BK + off);
 #pragma unroll
-            for (int b = 0; b < 4; ++b) bf[b] = *reinterpret_cast<const v4i *>(xs + b * 32 * BK + off);
+            for (int b = 0; b < kNB; ++b) bf[b] = *reinterpret_cast<const v4i *>(xs + b * 16 * BK + off);
         } else {
             const int c0 = kk * 4 + half * 2;
             const int off0 = lrow * BK + ((c0 ^ lsw) << 4);
@@ -290,39 +365,76 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         }
     };
 
+    // int8: one of the 16 fragments of a stage (0..7: weight blocks, 8..15:
+    // activation blocks) into set af / bf; `lp` is the stage's base plus this
+    // lane's offset (one address per stage, the blocks at immediate offsets).
+    auto read_frag_i8 = [&](const uint8_t *lp, auto idx_c, frag_t *af, frag_t *bf) {
+        constexpr int I = decltype(idx_c)::value;
+        if constexpr (kInt8) {
+            if constexpr (I < 8) af[I] = *reinterpret_cast<const v4i *>(lp + kOpBytes + (wn * 128 + I * 16) * BK);
+            else bf[I - 8] = *reinterpret_cast<const v4i *>(lp + (wm * 128 + (I - 8) * 16) * BK);
+        }
+    };
+
     // FIRST: the tile's first k-step, which starts the accumulators from an
     // inline-constant zero instead of zeroing 256 registers beforehand.
+    // One int8 MFMA, accumulator tied to its AGPRs.  Written as inline asm:
+    // with the builtin, the register allocator kept 64 separate 4-register
+    // accumulators in fixed registers only in part, and rotated the rest
+    // through other AGPRs and VGPRs inside the K loop (untied MFMAs, copies
+    // and s_nop waits).  The compiler does not see these as MFMAs, so the
+    // K loop's consumers of their results are covered explicitly: the
+    // loop's own MFMAs read an accumulator 64 MFMAs after writing it, and the
+    // epilogue starts after explicit wait states.  FIRST starts from zero
+    // (inline constant) instead of the accumulator.
+    auto mfma_i8 = [&](v4i &c, const v4i &a, const v4i &b, auto first_c) {
+        if constexpr (decltype(first_c)::value)
+            asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
+        else
+            asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+    };
     auto mfmas = [&](const frag_t *af, const frag_t *bf, auto first_c) {
         constexpr bool FIRST = decltype(first_c)::value;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
-            for (int mb = 0; mb < 4; ++mb) {
-                const acc_t c = FIRST ? acc_t{} : acc[nb][mb];
-                if constexpr (kInt8)
-                    acc[nb][mb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[nb], bf[mb], c, 0, 0, 0);
-                else
+            for (int mb = 0; mb < kNB; ++mb) {
+                if constexpr (kInt8) {
+                    mfma_i8(acc[nb][mb], af[nb], bf[mb], std::integral_constant<bool, FIRST>{});
+                } else {
+                    const acc_t c = FIRST ? acc_t{} : acc[nb][mb];
                     acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[nb], bf[mb], c, 0, 0, 0, 127, 0,
                                                                                   127);
+                }
             }
     };
 
-    // Interleave the memory instructions of a k-step with its 16 MFMAs so that
+    // Interleave the memory instructions of a k-step with its MFMAs so that
     // their issue (the LDS-DMA loads especially) overlaps MFMA execution
     // instead of stalling the wave in front of the matrix pipe.
-    constexpr int kDsPerStep = kInt8 ? 8 : 16;  // ds_read_b128 per fragment set
+    constexpr int kMfmas = kNB * kNB;  // MFMAs per k-step
+    constexpr int kDsPerStep = 16;     // ds_read_b128 per fragment set (both types)
+    // Where the reads and loads go among a k-step's MFMAs: e4m3 spreads both
+    // over its 16 MFMAs; int8 puts the next stage's 16 fragment reads (into
+    // the other fragment set) in the first half of its 64 short MFMAs and the
+    // refill loads in the second, so that the four waves leaving a barrier
+    // together do not queue 64 KB of reads at the LDS at once.
+    constexpr int kDsLo = 0, kDsHi = kInt8 ? kMfmas / 2 : kMfmas;
+    constexpr int kVmLo = kInt8 ? kMfmas / 2 : 0, kVmHi = kMfmas;
     auto interleave = [&](auto nvm_c) {
         constexpr int NVM = decltype(nvm_c)::value;
         [&]<int... I>(std::integer_sequence<int, I...>) {
             (([&] {
                  __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                 constexpr int ds = (I + 1) * kDsPerStep / 16 - I * kDsPerStep / 16;
+                 constexpr int di = I - kDsLo, dn = kDsHi - kDsLo;
+                 constexpr int ds = (I >= kDsLo && I < kDsHi) ? (di + 1) * kDsPerStep / dn - di * kDsPerStep / dn : 0;
                  if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0);  // DS reads
-                 constexpr int vm = (I + 1) * NVM / 16 - I * NVM / 16;
+                 constexpr int vi = I - kVmLo, vn = kVmHi - kVmLo;
+                 constexpr int vm = (I >= kVmLo && I < kVmHi) ? (vi + 1) * NVM / vn - vi * NVM / vn : 0;
                  if constexpr (vm > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm, 0);  // VMEM reads
              }()),
              ...);
-        }(std::make_integer_sequence<int, 16>{});
+        }(std::make_integer_sequence<int, kMfmas>{});
     };
 
     // Within a stage the fragments of k-step kk+1 are read while the MFMAs of
@@ -368,19 +480,50 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                      __builtin_amdgcn_sched_barrier(0);
                  } else {
                      // without this stage's earlier parts in flight, fewer may remain
-                     if (issue) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPending) : "memory");
-                     else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kPending - (kParts - 1) * kPerPart) : "memory");
-                     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                     if (issue) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPending));
+                     else __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPending - (kParts - 1) * kPerPart));
+                     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
                      // a bare barrier: __syncthreads() would add a release fence,
                      // i.e. a wait for every load in flight, prefetches included
                      asm volatile("s_barrier" ::: "memory");
                      __builtin_amdgcn_sched_barrier(0);
-                     if (issue)
-                         load_part(refill, std::integral_constant<int, kk>{}, std::integral_constant<int, kParts>{});
-                     read_frags(nxt, 0, fa[P ^ 1], fb[P ^ 1]);
-                     mfmas(fa[P], fb[P], std::integral_constant<bool, FIRST && S == 0 && kk == 0>{});
-                     interleave(std::integral_constant<int, kPerPart>{});
-                     __builtin_amdgcn_sched_barrier(0);
+                     if constexpr (kInt8) {
+                         // 16 groups of 4 MFMAs (block row nb = g / 2, block columns
+                         // 4 (g % 2) .. + 3) in program order, each followed by its
+                         // share of the next stage's fragment reads (into the other
+                         // set) and of the refill loads
+                         int off = foff;
+                         asm volatile("" : "+v"(off));
+                         const uint8_t *lp = nxt + off;
+                         [&]<int... G>(std::integer_sequence<int, G...>) {
+                             (([&] {
+                                  constexpr int g = G;
+                                  constexpr auto first = std::integral_constant<bool, FIRST && S == 0>{};
+#pragma unroll
+                                  for (int j = 0; j < 4; ++j)
+                                      mfma_i8(acc[g / 2][(g % 2) * 4 + j], fa[P][g / 2], fb[P][(g % 2) * 4 + j], first);
+                                  [&]<int... R>(std::integer_sequence<int, R...>) {
+                                      (read_frag_i8(lp, std::integral_constant<int, i8_read_first(g) + R>{}, fa[P ^ 1],
+                                                    fb[P ^ 1]),
+                                       ...);
+                                  }(std::make_integer_sequence<int, i8_reads_after(g)>{});
+                                  if constexpr (i8_loads_after(g)) {
+                                      if (issue)
+                                          load_part(refill, std::integral_constant<int, i8_load_part(g)>{},
+                                                    std::integral_constant<int, kLoadsPerStage>{});
+                                  }
+                                  __builtin_amdgcn_sched_barrier(0);
+                              }()),
+                              ...);
+                         }(std::make_integer_sequence<int, 16>{});
+                     } else {
+                         if (issue)
+                             load_part(refill, std::integral_constant<int, kk>{}, std::integral_constant<int, kParts>{});
+                         read_frags(nxt, 0, fa[P ^ 1], fb[P ^ 1]);
+                         mfmas(fa[P], fb[P], std::integral_constant<bool, FIRST && S == 0 && kk == 0>{});
+                         interleave(std::integral_constant<int, kPerPart>{});
+                         __builtin_amdgcn_sched_barrier(0);
+                     }
                  }
              }()),
              ...);
@@ -425,9 +568,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     asm volatile("s_barrier" ::: "memory");
 
     // bf16 epilogue of one tile: y = bf16(acc * sx[m] * sw (+ u . l2^T) + bias[n]).
+    // Every lane holds, per output block, groups ("quads") of 4 consecutive
+    // columns of one row:
+    //   int8 (16x16 blocks): block (nb, mb), registers 0..3 -> row
+    //     mb * 16 + (l & 15), columns nb * 16 + 4 (l >> 4) + 0..3;
+    //   e4m3 (32x32 blocks): block (nb, mb), registers 4q..4q+3 -> row
+    //     mb * 32 + (l & 31), columns nb * 32 + 8q + 4 (l >> 5) + 0..3.
     // Result rows go through this wave's LDS staging area (32 rows x 256 B,
-    // 16-byte chunks XOR-swizzled by row) and leave as 16-byte stores that
-    // cover whole 256-byte row segments.
+    // 16-byte chunks XOR-swizzled by row) in four passes of 32 rows and leave
+    // as 16-byte stores that cover whole 256-byte row segments.
+    constexpr int kPassBlocks = 32 / kBlk;  // block rows per 32-row pass
     auto bf16_epilogue = [&](auto interior_c, int mw, int nw) {
         constexpr bool kIn = decltype(interior_c)::value;
         uint16_t *out = static_cast<uint16_t *>(p.out);
@@ -437,37 +587,38 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         // loop and spill).
         int el = lane;
         asm volatile("" : "+v"(el));
-        const int erow = el & 31, ehalf = el >> 5;
+        const int brow = el & (kBlk - 1);  // the lane's row within a block
+        const int cq = 4 * (el / kBlk);    // the lane's first column within a quad group
         constexpr bool kCol = EPI == kEpiColScale;
-        float tm[4];
-        uint2 bias2[4][4];
-        v4f swc[kCol ? 4 : 1][4];  // per-channel weight scales of columns nb * 32 + 8 j + 4 half + i
+        float tm[kNB];
+        uint2 bias2[kNB][kQuads];
+        v4f swc[kCol ? kNB : 1][kCol ? kQuads : 1];  // per-channel weight scales of the lane's quads
         const float sw = kCol ? 1.0f : p.sw[0];
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-            const int m = mw + mb * 32 + erow;
-            if constexpr (kIn) tm[mb] = *reinterpret_cast<const float *>(ob + kEpiSx + (mb * 32 + erow) * 4) * sw;
+        for (int mb = 0; mb < kNB; ++mb) {
+            const int m = mw + mb * kBlk + brow;
+            if constexpr (kIn) tm[mb] = *reinterpret_cast<const float *>(ob + kEpiSx + (mb * kBlk + brow) * 4) * sw;
             else tm[mb] = m < M ? p.sx[m] * sw : 0.0f;
         }
         if constexpr (kCol) {
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
+            for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int n = nw + nb * 32 + 8 * j + 4 * ehalf;
+                for (int q = 0; q < kQuads; ++q) {
+                    const int n = nw + nb * kBlk + 8 * q + cq;
                     if (kIn || ((N & 3) == 0 && n < N)) {
-                        swc[nb][j] = *reinterpret_cast<const v4f *>(p.sw + n);
+                        swc[nb][q] = *reinterpret_cast<const v4f *>(p.sw + n);
                     } else {
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) swc[nb][j][i] = n + i < N ? p.sw[n + i] : 0.0f;
+                        for (int i = 0; i < 4; ++i) swc[nb][q][i] = n + i < N ? p.sw[n + i] : 0.0f;
                     }
                 }
         }
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int n = nw + nb * 32 + 8 * j + 4 * ehalf;
+            for (int q = 0; q < kQuads; ++q) {
+                const int n = nw + nb * kBlk + 8 * q + cq;
                 uint2 b = make_uint2(0u, 0u);
                 if (p.bias) {
                     if constexpr (kIn) {
@@ -481,7 +632,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                         b = make_uint2(w[0] | (w[1] << 16), w[2] | (w[3] << 16));
                     }
                 }
-                bias2[nb][j] = b;
+                bias2[nb][q] = b;
             }
         constexpr bool kLr32 = EPI == kEpiLowRank32;
         constexpr bool kLrBatch = kLr32 && kInt8;
@@ -519,86 +670,107 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
             if constexpr (kLrBatch) {
                 // int8: scale the accumulators in place while the operands land
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb)
+                for (int mb = 0; mb < kNB; ++mb)
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb) {
-                        v16f t;
+                    for (int nb = 0; nb < kNB; ++nb) {
+                        const v4i c = blk(nb, mb);
+                        v4f t;
 #pragma unroll
-                        for (int e = 0; e < 16; ++e) t[e] = (float)acc[nb][mb][e] * tm[mb];
-                        acc[nb][mb] = __builtin_bit_cast(acc_t, t);
+                        for (int e = 0; e < 4; ++e) t[e] = (float)c[e] * tm[mb];
+                        set_blk(nb, mb, __builtin_bit_cast(blk_t, t));
                     }
             }
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             asm volatile("s_barrier" ::: "memory");
         }
+        // int8 low-rank: the l2 fragments of the wave's 8 column blocks (rows
+        // n of l2, the lane's 8 of up to 32 rank columns; zero past r)
+        v8bf al2[kLrBatch ? kNB : 1];
+        if constexpr (kLrBatch) {
+            const int j0 = (el >> 4) * 8;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
+            for (int nb = 0; nb < kNB; ++nb) {
+                al2[nb] = v8bf{};
+                if (j0 < p.r) al2[nb] = *reinterpret_cast<const v8bf *>(lb + ((wn * 128 + nb * 16 + brow) * p.r + j0) * 2);
+            }
+        }
+#pragma unroll
+        for (int ps = 0; ps < 4; ++ps) {
             if constexpr (kLrBatch) {
-                // u . l2^T of the 4 blocks of this block row from the staged
-                // rows, the MFMAs interleaved over the blocks so that they
-                // issue back to back rather than each waiting on the last
-                const int urow = wm * 128 + mb * 32 + erow;
+                // u . l2^T of this pass's block rows from the staged rows on the
+                // 16x16x32 bf16 MFMA (u as hi + lo), interleaved over the
+                // column blocks so that consecutive MFMAs are independent
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    if (ks * 16 >= p.rp) break;
-                    const int j0 = ks * 16 + ehalf * 8;
-                    v8bf a[4];
+                for (int qb = 0; qb < kPassBlocks; ++qb) {
+                    const int mb = ps * kPassBlocks + qb;
+                    const int j0 = (el >> 4) * 8;
+                    const int urow = wm * 128 + mb * 16 + brow;
+                    v8bf uh = v8bf{}, ul = v8bf{};
+                    if (j0 < p.rp) {
+                        uh = *reinterpret_cast<const v8bf *>(ub + (urow * p.rp + j0) * 2);
+                        ul = *reinterpret_cast<const v8bf *>(ub + half_bytes + (urow * p.rp + j0) * 2);
+                    }
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb)
-                        a[nb] = *reinterpret_cast<const v8bf *>(lb + ((wn * 128 + nb * 32 + erow) * p.r + j0) * 2);
-                    const v8bf uh = *reinterpret_cast<const v8bf *>(ub + (urow * p.rp + j0) * 2);
-                    const v8bf ul = *reinterpret_cast<const v8bf *>(ub + half_bytes + (urow * p.rp + j0) * 2);
+                    for (int nb = 0; nb < kNB; ++nb)
+                        set_blk(nb, mb, __builtin_bit_cast(blk_t, __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            al2[nb], uh, __builtin_bit_cast(v4f, blk(nb, mb)), 0, 0, 0)));
 #pragma unroll
-                    for (int nb = 0; nb < 4; ++nb)
-                        acc[nb][mb] = __builtin_bit_cast(acc_t, __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            a[nb], uh, __builtin_bit_cast(v16f, acc[nb][mb]), 0, 0, 0));
-#pragma unroll
-                    for (int nb = 0; nb < 4; ++nb)
-                        acc[nb][mb] = __builtin_bit_cast(acc_t, __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                            a[nb], ul, __builtin_bit_cast(v16f, acc[nb][mb]), 0, 0, 0));
+                    for (int nb = 0; nb < kNB; ++nb)
+                        set_blk(nb, mb, __builtin_bit_cast(blk_t, __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            al2[nb], ul, __builtin_bit_cast(v4f, blk(nb, mb)), 0, 0, 0)));
                 }
             }
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-                v16f v;
-                if constexpr (kLrBatch) {
-                    v = __builtin_bit_cast(v16f, acc[nb][mb]);
-                } else {
+            for (int qb = 0; qb < kPassBlocks; ++qb) {
+                const int mb = ps * kPassBlocks + qb;
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) v[e] = (float)acc[nb][mb][e] * tm[mb];
-                }
-                if constexpr (EPI == kEpiLowRank) v = low_rank_add(p, v, nw + nb * 32, mw + mb * 32, erow, ehalf);
-                if constexpr (kLr32 && !kLrBatch) {
-                    // e4m3: u . l2^T of this block from the staged rows (the
-                    // interleaved form above needs more registers than this
-                    // instantiation has, and was slower)
-                    const int urow = wm * 128 + mb * 32 + erow, lrow2 = wn * 128 + nb * 32 + erow;
+                for (int nb = 0; nb < kNB; ++nb) {
+                    typedef typename std::conditional<kInt8, v4f, v16f>::type vals_t;
+                    vals_t v;
+                    const blk_t c = blk(nb, mb);
+                    if constexpr (kLrBatch) {
+                        v = __builtin_bit_cast(vals_t, c);
+                    } else {
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        if (ks * 16 >= p.rp) break;
-                        const int j0 = ks * 16 + ehalf * 8;
-                        const v8bf a = *reinterpret_cast<const v8bf *>(lb + (lrow2 * p.r + j0) * 2);
-                        const v4u uh = *reinterpret_cast<const v4u *>(ub + (urow * p.rp + j0) * 2);
-                        const v4u ul = *reinterpret_cast<const v4u *>(ub + half_bytes + (urow * p.rp + j0) * 2);
-                        v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, uh), v, 0, 0, 0);
-                        v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, ul), v, 0, 0, 0);
+                        for (int e = 0; e < 4 * kQuads; ++e) v[e] = (float)c[e] * tm[mb];
                     }
-                }
-                if constexpr (kCol) {
+                    if constexpr (EPI == kEpiLowRank) {
+                        if constexpr (kInt8) v = low_rank_add16(p, v, nw + nb * 16, mw + mb * 16, brow, el);
+                        else v = low_rank_add(p, v, nw + nb * 32, mw + mb * 32, brow, el >> 5);
+                    }
+                    if constexpr (kLr32 && !kLrBatch) {
+                        // e4m3: u . l2^T of this block from the staged rows (the
+                        // interleaved form above needs more registers than this
+                        // instantiation has, and was slower)
+                        const int urow = wm * 128 + mb * 32 + brow, lrow2 = wn * 128 + nb * 32 + brow;
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) v[e] *= swc[nb][e / 4][e % 4];
-                }
+                        for (int ks = 0; ks < 2; ++ks) {
+                            if (ks * 16 >= p.rp) break;
+                            const int j0 = ks * 16 + (el >> 5) * 8;
+                            const v8bf a = *reinterpret_cast<const v8bf *>(lb + (lrow2 * p.r + j0) * 2);
+                            const v4u uh = *reinterpret_cast<const v4u *>(ub + (urow * p.rp + j0) * 2);
+                            const v4u ul = *reinterpret_cast<const v4u *>(ub + half_bytes + (urow * p.rp + j0) * 2);
+                            v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, uh), v, 0, 0, 0);
+                            v = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, __builtin_bit_cast(v8bf, ul), v, 0, 0, 0);
+                        }
+                    }
+                    if constexpr (kCol) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint2 bb = bias2[nb][j];
-                    const float y0 = v[4 * j] + bf16_bits_to_f32(bb.x & 0xFFFFu);
-                    const float y1 = v[4 * j + 1] + bf16_bits_to_f32(bb.x >> 16);
-                    const float y2 = v[4 * j + 2] + bf16_bits_to_f32(bb.y & 0xFFFFu);
-                    const float y3 = v[4 * j + 3] + bf16_bits_to_f32(bb.y >> 16);
-                    const int col = nb * 32 + 8 * j + 4 * ehalf;  // bf16 column within the wave tile
-                    const int chunk = (col >> 3) ^ (erow & 15);
-                    *reinterpret_cast<uint2 *>(ob + erow * 256 + chunk * 16 + (col & 7) * 2) =
-                        make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+                        for (int e = 0; e < 4 * kQuads; ++e) v[e] *= swc[nb][e / 4][e % 4];
+                    }
+#pragma unroll
+                    for (int q = 0; q < kQuads; ++q) {
+                        const uint2 bb = bias2[nb][q];
+                        const float y0 = v[4 * q] + bf16_bits_to_f32(bb.x & 0xFFFFu);
+                        const float y1 = v[4 * q + 1] + bf16_bits_to_f32(bb.x >> 16);
+                        const float y2 = v[4 * q + 2] + bf16_bits_to_f32(bb.y & 0xFFFFu);
+                        const float y3 = v[4 * q + 3] + bf16_bits_to_f32(bb.y >> 16);
+                        const int row = qb * kBlk + brow;           // row within the pass
+                        const int col = nb * kBlk + 8 * q + cq;     // bf16 column within the wave tile
+                        const int chunk = (col >> 3) ^ (row & 15);
+                        *reinterpret_cast<uint2 *>(ob + row * 256 + chunk * 16 + (col & 7) * 2) =
+                            make_uint2(pack_bf16x2(y0, y1), pack_bf16x2(y2, y3));
+                    }
                 }
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -607,7 +779,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
             for (int it = 0; it < 8; ++it) {
                 const int r = it * 4 + (el >> 4), c = el & 15;
                 const v4u d = *reinterpret_cast<const v4u *>(ob + r * 256 + ((c ^ (r & 15)) << 4));
-                const int m = mw + mb * 32 + r, n = nw + c * 8;
+                const int m = mw + ps * 32 + r, n = nw + c * 8;
                 uint16_t *dst = out + (size_t)m * N + n;
                 if constexpr (kIn) {
                     __builtin_nontemporal_store(d, reinterpret_cast<v4u *>(dst));
@@ -659,28 +831,34 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         }
 
         // --------------------------------------------------------- epilogue
+        // int8: the last MFMAs were inline asm, which the compiler's hazard
+        // tracking does not see; give their results the wait states an MFMA
+        // result needs before other instructions read it (24 >= the 16x16x64
+        // requirement) before the epilogue touches the accumulators.
+        if constexpr (kInt8) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
         // Block (nb, mb), register 4j+i holds output row m = mbase + (l & 31)
         // and column n = nbase + 8j + 4(l >> 5) + i.
         if constexpr (EPI == kEpiI32) {
             int32_t *out = static_cast<int32_t *>(p.out);
+            const int brow = lane & (kBlk - 1), cq = 4 * (lane / kBlk);
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
+            for (int nb = 0; nb < kNB; ++nb)
 #pragma unroll
-                for (int mb = 0; mb < 4; ++mb) {
-                    const int m = mw + mb * 32 + lrow;
+                for (int mb = 0; mb < kNB; ++mb) {
+                    const int m = mw + mb * kBlk + brow;
                     if (m >= M) continue;
+                    const blk_t c = blk(nb, mb);
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int n = nw + nb * 32 + 8 * j + 4 * half;
+                    for (int q = 0; q < kQuads; ++q) {
+                        const int n = nw + nb * kBlk + 8 * q + cq;
                         int32_t *dst = out + (size_t)m * N + n;
                         if ((N & 3) == 0 && n + 3 < N) {
-                            v4i v = {(int)acc[nb][mb][4 * j], (int)acc[nb][mb][4 * j + 1],
-                                     (int)acc[nb][mb][4 * j + 2], (int)acc[nb][mb][4 * j + 3]};
+                            v4i v = {(int)c[4 * q], (int)c[4 * q + 1], (int)c[4 * q + 2], (int)c[4 * q + 3]};
                             *reinterpret_cast<v4i *>(dst) = v;
                         } else {
 #pragma unroll
                             for (int i = 0; i < 4; ++i)
-                                if (n + i < N) dst[i] = (int)acc[nb][mb][4 * j + i];
+                                if (n + i < N) dst[i] = (int)c[4 * q + i];
                         }
                     }
                 }

@@ -5,10 +5,10 @@
 // operand values).
 //
 // One workgroup of 4 waves per CU (one wave per SIMD, as the GEMM).  Every
-// wave takes two sets of 4 A and 4 B fragments of v_mfma_i32_32x32x32_i8
-// from the given operand bytes and loops over the 16 products of a 4x4 block
-// of 32x32 accumulators, alternating the sets -- the GEMM's k-step without
-// its memory traffic.
+// wave takes 8 A and 8 B fragments of v_mfma_i32_16x16x64_i8 (the GEMM's int8
+// MFMA) from the given operand bytes and loops over the 64 products of an
+// 8x8 block of 16x16 accumulators -- the GEMM's k-step without its memory
+// traffic.
 //
 // A second probe checks the hardware e4m3 conversion the quantizers use
 // (clamp to +-448 with v_med3_f32, then v_cvt_pk_fp8_f32 with RNE) on every
@@ -26,36 +26,32 @@ __global__ __launch_bounds__(256) void probe_mfma_i8_kernel(const int8_t *__rest
                                                             int64_t pairs, int32_t *__restrict__ sink) {
     const int lane = threadIdx.x & 63;
     const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);  // global wave index
-    v4i fa[2][4], fb[2][4];
+    v4i fa[8], fb[8];
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int i = 0; i < 8; ++i) {
+        const int off = ((gw * 8 + i) * 1024 + lane * 16) % kProbeBytes;
+        fa[i] = *reinterpret_cast<const v4i *>(a + off);
+        fb[i] = *reinterpret_cast<const v4i *>(b + off);
+    }
+    v4i acc[8][8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int off = ((gw * 8 + s * 4 + i) * 1024 + lane * 16) % kProbeBytes;
-            fa[s][i] = *reinterpret_cast<const v4i *>(a + off);
-            fb[s][i] = *reinterpret_cast<const v4i *>(b + off);
-        }
-    v16i acc[4][4];
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = v16i{};
+        for (int j = 0; j < 8; ++j) acc[i][j] = v4i{};
     for (int64_t it = 0; it < pairs; ++it) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
+        for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < 8; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
     int32_t x = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int e = 0; e < 16; ++e) x ^= acc[i][j][e];
+            for (int e = 0; e < 4; ++e) x ^= acc[i][j][e];
     sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = x;
 }
 
