@@ -92,7 +92,8 @@ def _kernel_hash():
 
 
 def _traffic_from_profile(kernel_hash):
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter summary,
+    """L2-to-fabric bytes per GEMM launch (FETCH_SIZE + WRITE_SIZE, calibrated)
+    from the committed rocprofv3 counter summary,
     if it was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", "gemm_int8_M4096_N12288_K3072_traffic.txt")
     if not os.path.exists(path):
@@ -106,7 +107,7 @@ def _traffic_from_profile(kernel_hash):
     if vals.get("kernel_source_hash") != kernel_hash:
         return None
     try:
-        return float(vals["hbm_bytes_per_launch"])
+        return float(vals["l2_fabric_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
 
