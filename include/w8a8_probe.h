@@ -49,6 +49,14 @@ w8a8_status w8a8_probe_mfma_i8(const void *a, const void *b, int64_t pairs, int3
  */
 w8a8_status w8a8_probe_cvt_e4m3(uint32_t first_bits, int64_t n, uint8_t *codes, hipStream_t stream);
 
+/*
+ * Tile width along N (256 or 192) that w8a8_linear and
+ * w8a8_linear_backward_dx choose for an M x N output on the current device
+ * (every other product uses 256), so that a test can tell which kernel a
+ * shape exercises.  Returns 0 for M or N below 1.  Enqueues nothing.
+ */
+int w8a8_probe_gemm_tile_n(int64_t M, int64_t N);
+
 #ifdef __cplusplus
 }
 #endif

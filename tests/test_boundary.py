@@ -4,6 +4,7 @@ error paths and zero-size no-ops are called (they touch no device memory)."""
 import ctypes
 
 import pytest
+import torch
 
 import w8a8_quantized_linear_quant_amd as w8
 
@@ -18,7 +19,7 @@ def test_exports_match_header():
     names = w8.exported_names_in_header()
     assert len(names) == 20
     probe = w8.exported_names_in_header(w8.PROBE_HEADER)
-    assert probe == ["w8a8_probe_cvt_e4m3", "w8a8_probe_mfma_i8", "w8a8_probe_sink_count"]
+    assert probe == ["w8a8_probe_cvt_e4m3", "w8a8_probe_gemm_tile_n", "w8a8_probe_mfma_i8", "w8a8_probe_sink_count"]
     for n in names + probe:
         assert hasattr(lib, n), n
 
@@ -33,6 +34,19 @@ def test_probe_rejects():
     assert lib.w8a8_probe_mfma_i8(A, A, -1, A, NULL) == INVALID
     assert lib.w8a8_probe_mfma_i8(MIS, A, 1, A, NULL) == ALIGN
     assert lib.w8a8_probe_mfma_i8(A, A, 0, A, NULL) == OK
+    assert lib.w8a8_probe_gemm_tile_n(0, 3072) == 0
+    assert lib.w8a8_probe_gemm_tile_n(8192, -1) == 0
+
+
+def test_tile_width_model_on_256_cus():
+    # without a device the library prices tile widths for 256 CUs
+    if torch.cuda.is_available():
+        pytest.skip("the GPU's own CU count decides; covered by the GPU tests")
+    assert lib.w8a8_probe_gemm_tile_n(8192, 3072) == 192    # 384 tiles of 256: 1.5 rounds
+    assert lib.w8a8_probe_gemm_tile_n(4349, 4100) == 192
+    assert lib.w8a8_probe_gemm_tile_n(4096, 12288) == 256   # whole rounds
+    assert lib.w8a8_probe_gemm_tile_n(4608, 3072) == 256    # one round
+    assert lib.w8a8_probe_gemm_tile_n(1, 1) == 256
 
 
 def test_status_strings():

@@ -375,6 +375,48 @@ def test_backward_dx_ragged(qt, M, N, K):
         assert_frobenius(bf16_host(dx), ref, "e4m3 dX ragged")
 
 
+def _cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+@pytest.mark.parametrize("qt", [INT8, FP8])
+@pytest.mark.parametrize("M,N,K", [(4349, 4096, 512), (4349, 4100, 80)])
+def test_linear_192_wide_tiles(qt, M, N, K):
+    """Shapes whose 256-wide tiles would leave a partial second round, so the
+    product takes 192-wide tiles (on a 256-CU device): the whole output
+    against the oracle, M ragged, N a multiple of 8 (unchecked epilogue of
+    interior tiles) or not (checked epilogue), K a multiple of the stage ring
+    or with a tail."""
+    if _cus() != 256:
+        pytest.skip("tile-width choice assumes 256 CUs")
+    assert W8.probe_gemm_tile_n(M, N) == 192
+    _say(f"linear 192-wide tiles qt={qt} M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + 3 * N + K + qt)
+    x = workloads.activations_bf16(rng, M, K, outliers=4)
+    w = workloads.normal_bf16(rng, (N, K), 0.02)
+    b = workloads.normal_bf16(rng, (N,), 0.02)
+    got = _gpu_linear(x, w, b, qt)
+    xq, sx = oracle.quant_act_rowwise(qt, x)
+    wq, _, sw = oracle.quant_weight_tensorwise(qt, w)
+    ref = oracle.linear(qt, xq, sx, wq, sw, b)
+    assert_bf16_close(got, ref, f"192-wide qt={qt}")
+    if qt == FP8:
+        assert_frobenius(got, ref, "192-wide e4m3 linear")
+
+
+def test_tile_width_choice():
+    """256-wide tiles wherever they fill whole rounds or a single round; 192
+    for the dX product of the training step (M8192, N3072: 1.5 rounds of
+    256-wide tiles)."""
+    if _cus() != 256:
+        pytest.skip("tile-width choice assumes 256 CUs")
+    assert W8.probe_gemm_tile_n(8192, 3072) == 192     # dX [8192, 3072]
+    assert W8.probe_gemm_tile_n(4096, 12288) == 256    # 768 tiles, 3 rounds
+    assert W8.probe_gemm_tile_n(8192, 12288) == 256    # 1536 tiles, 6 rounds
+    assert W8.probe_gemm_tile_n(4608, 3072) == 256     # 216 tiles, one round
+    assert W8.probe_gemm_tile_n(4608, 12288) == 256
+
+
 def test_int8_step_backward_sampled():
     _say("int8 train step dX at M=8192 N=12288 K=3072 (sampled rows and columns)")
     d = workloads.fp8_step()

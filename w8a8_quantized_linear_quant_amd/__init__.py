@@ -19,6 +19,7 @@ the current stream.  The functions carry the C names:
   gguf_a8_linear                8-bit product with per-channel weight scales -> bf16
   probe_mfma_i8                 diagnostic: sustained int8 MFMA loop (include/w8a8_probe.h)
   probe_cvt_e4m3                diagnostic: the hardware e4m3 conversion on consecutive f32 bit patterns
+  probe_gemm_tile_n             diagnostic: the tile width along N w8a8_linear picks for an M x N output
 
 Codes are torch.int8 (int8) or torch.float8_e4m3fn (e4m3); bf16 tensors are
 torch.bfloat16; scales are float32.  Output tensors may be passed in (`out=`)
@@ -76,6 +77,7 @@ def _load_library():
         "w8a8_probe_sink_count": (I64, []),
         "w8a8_probe_mfma_i8": (I, [P, P, I64, P, P]),
         "w8a8_probe_cvt_e4m3": (I, [ctypes.c_uint32, I64, P, P]),
+        "w8a8_probe_gemm_tile_n": (I, [I64, I64]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -472,3 +474,9 @@ def probe_cvt_e4m3(first_bits, n, out=None, device=None):
     codes = _buf(out, n, torch.uint8, dev, "out", alloc=16)
     _check(_lib.w8a8_probe_cvt_e4m3(ctypes.c_uint32(first_bits), n, _ptr(codes), _stream(dev)))
     return codes[:n]
+
+
+def probe_gemm_tile_n(M, N):
+    """Tile width along N (256 or 192) that w8a8_linear and
+    w8a8_linear_backward_dx take for an M x N output on the current device."""
+    return int(_lib.w8a8_probe_gemm_tile_n(int(M), int(N)))

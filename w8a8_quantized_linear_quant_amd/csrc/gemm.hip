@@ -35,12 +35,13 @@
 
 #include <atomic>
 
+#include "../../include/w8a8_probe.h"
 #include "internal.hpp"
 
 namespace w8a8 {
 namespace {
 
-constexpr int BM = 256, BN = 256;
+constexpr int BM = 256;  // tile height along M (the tile width along N is a kernel parameter)
 constexpr int kThreads = 256;
 #ifndef W8A8_GEMM_GROUP_M
 #define W8A8_GEMM_GROUP_M 4
@@ -60,8 +61,8 @@ constexpr int kOpBytes = 256 * BK;         // one operand tile per stage
 constexpr int kStageBytes = 2 * kOpBytes;  // X tile then W tile
 constexpr int kChunks = BK / 16;           // 16-byte chunks per row
 constexpr int kRowsPerLoad = 64 / kChunks; // rows one wave-wide 1 KB load covers
-constexpr int kLoadsPerOp = 64 / kRowsPerLoad;  // per wave and operand: 64 rows
-constexpr int kLoadsPerStage = 2 * kLoadsPerOp;
+constexpr int kLoadsPerOp = 64 / kRowsPerLoad;  // per wave and operand: 64 rows (of 256)
+constexpr int kLoadsPerStage = 2 * kLoadsPerOp; // the most a stage issues per wave (256-wide tile)
 constexpr int kImmLoads = kLoadsPerOp < 4 ? kLoadsPerOp : 4;  // loads per M0 value (immediate offsets < 4 KB)
 constexpr int kOutWaveBytes = 32 * 256;    // epilogue staging per wave
 static_assert(NST >= 3 && NST <= 4, "3..4 LDS stages");
@@ -87,37 +88,18 @@ __device__ __forceinline__ int swz(int row) {
     else return ((row >> 1) ^ (row >> 2)) & 3;
 }
 
-// Placement of the int8 stage's memory instructions among its 16 groups of
-// 4 MFMAs: after group g, fragment reads i8_read_first(g) ..
-// + i8_reads_after(g) - 1 of the next stage, and one refill load (part
-// i8_load_part(g) of the stage's loads) if i8_loads_after(g).
-#ifndef W8A8_GEMM_I8_SCHED
-#define W8A8_GEMM_I8_SCHED 2
-#endif
-constexpr int i8_reads_after(int g) {
-    if (W8A8_GEMM_I8_SCHED == 0) return g < 8 ? 2 : 0;    // reads in the first half
-    if (W8A8_GEMM_I8_SCHED == 1) return g == 0 ? 16 : 0;  // reads together after the first group
-    return 1;                                             // one read per group (2, 3)
-}
-constexpr int i8_read_first(int g) {
-    int n = 0;
-    for (int i = 0; i < g; ++i) n += i8_reads_after(i);
-    return n;
-}
-constexpr bool i8_loads_after(int g) {
-    if (W8A8_GEMM_I8_SCHED == 2) return g % 2 == 1;      // one load per two groups
-    return g >= 8;                                        // loads in the second half (0, 1, 3)
-}
-constexpr int i8_load_part(int g) {
-    int n = 0;
-    for (int i = 0; i < g; ++i) n += i8_loads_after(i) ? 1 : 0;
-    return n;
-}
+// Even spread of `total` items over `groups` slots: slot g takes items
+// spread_first(g) .. + spread_count(g) - 1.  The int8 stage places its next-
+// stage fragment reads and its refill loads this way among its groups of 4
+// MFMAs.
+constexpr int spread_first(int g, int total, int groups) { return g * total / groups; }
+constexpr int spread_count(int g, int total, int groups) { return (g + 1) * total / groups - g * total / groups; }
 
 struct TileCoord {
     int m0, n0;
 };
 
+template <int BNT>
 __device__ __forceinline__ TileCoord tile_coord(int tile, int tiles_m, int tiles_n) {
     const int nt = tiles_m * tiles_n;
     // XCD-major renumbering: hardware sends workgroup b to XCD b % 8, and a
@@ -134,7 +116,7 @@ __device__ __forceinline__ TileCoord tile_coord(int tile, int tiles_m, int tiles
     const int in = t - g * group;
     TileCoord c;
     c.m0 = (first_m + in % gm) * BM;
-    c.n0 = (in / gm) * BN;
+    c.n0 = (in / gm) * BNT;
     return c;
 }
 
@@ -194,8 +176,17 @@ __device__ __forceinline__ v4f low_rank_add16(const GemmArgs &p, v4f v, int nbas
 // TAIL: K is not a multiple of BK * NST, so some stages reach past K and
 // need per-lane range checks; otherwise every stage is whole and the stage's
 // K offset travels in the instruction's scalar offset.
-template <int QT, int EPI, bool TAIL>
+// BNT: tile width along N, 256 (wave tiles 128 x 128) or 192 (128 x 96, for
+// shapes whose 256-wide tiles would leave the last round of CUs half idle;
+// bf16 epilogue only).
+template <int QT, int EPI, bool TAIL, int BNT>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m, int tiles_n) {
+    static_assert(BNT == 256 || (BNT == 192 && EPI == kEpiBf16), "192-wide tiles: bf16 epilogue only");
+    constexpr int kWN = BNT / 2;                 // wave tile width along N
+    constexpr int kRowsW = BNT / 4;              // weight rows each wave loads per stage
+    constexpr int kLoadsW = kRowsW / kRowsPerLoad;
+    constexpr int kLoads = kLoadsPerOp + kLoadsW;  // loads per wave and stage
+    static_assert(kRowsW % kRowsPerLoad == 0, "whole weight loads per wave");
     // One distinct array per stage, so the compiler can tell the LDS-DMA writes
     // into one stage from the fragment reads of another and does not wait for
     // the former before the latter.
@@ -229,15 +220,18 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     // tile, kRowsPerLoad rows (1 KB) per instruction; lane l lands at LDS byte
     // 16 l of that KB: row l / kChunks, physical chunk l % kChunks, which holds
     // logical chunk (l % kChunks) ^ swz(row).
-    int goff[kLoadsPerOp], gcol[kLoadsPerOp];
+    // Loads 0 .. kLoadsPerOp - 1 of a stage fill the wave's 64 activation rows,
+    // the rest its kRowsW weight rows.
+    int goff[kLoads], gcol[kLoads];
 #pragma unroll
-    for (int i = 0; i < kLoadsPerOp; ++i) {
-        const int row = wave * 64 + i * kRowsPerLoad + lane / kChunks;
+    for (int j = 0; j < kLoads; ++j) {
+        const int i = j < kLoadsPerOp ? j : j - kLoadsPerOp;
+        const int row = (j < kLoadsPerOp ? wave * 64 : wave * kRowsW) + i * kRowsPerLoad + lane / kChunks;
         const int c = (lane % kChunks) ^ swz(row);
-        gcol[i] = c * 16;
+        gcol[j] = c * 16;
         // the instruction's immediate offset (i KB, see load_part) is added to
         // the global address as well as to the LDS address; take it back out
-        goff[i] = row * K + c * 16 - (i % kImmLoads) * 1024;
+        goff[j] = row * K + c * 16 - (i % kImmLoads) * 1024;
     }
 
     // ---- load cursor: the stage ring runs ahead across tile boundaries, so
@@ -251,9 +245,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         int rows_x = 0, rows_w = 0;
         size_t bx = 0, bw = 0;
         if (ld_tile < ntiles) {
-            const TileCoord c = tile_coord(ld_tile, tiles_m, tiles_n);
+            const TileCoord c = tile_coord<BNT>(ld_tile, tiles_m, tiles_n);
             rows_x = min(M - c.m0, BM);
-            rows_w = min(N - c.n0, BN);
+            rows_w = min(N - c.n0, BNT);
             bx = (size_t)c.m0 * K;
             bw = (size_t)c.n0 * K;
         }
@@ -269,23 +263,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     // instructions stalls the issuing wave.
     auto load_part = [&](uint8_t *stage, auto part_c, auto np_c) {
         constexpr int P = decltype(part_c)::value, NP = decltype(np_c)::value;
-        constexpr int lo = P * kLoadsPerStage / NP, hi = (P + 1) * kLoadsPerStage / NP;
+        constexpr int lo = P * kLoads / NP, hi = (P + 1) * kLoads / NP;
         const int k0 = ld_kt * BK;
         const bool full = !TAIL || k0 + BK <= K;
         [&]<int... J>(std::integer_sequence<int, J...>) {
             (([&] {
                  constexpr int j = lo + J;
-                 constexpr int i = j % kLoadsPerOp;
+                 constexpr bool kX = j < kLoadsPerOp;
+                 constexpr int i = kX ? j : j - kLoadsPerOp;
                  constexpr int grp = i / kImmLoads, imm = (i % kImmLoads) * 1024;
-                 uint8_t *m0 = stage + (j < kLoadsPerOp ? 0 : kOpBytes) + wave * 64 * BK + grp * kImmLoads * 1024;
+                 uint8_t *m0 = stage + (kX ? wave * 64 * BK : kOpBytes + wave * kRowsW * BK) + grp * kImmLoads * 1024;
                  if constexpr (TAIL) {
-                     const int o = full ? goff[i] + k0 : (k0 + gcol[i] < K ? goff[i] + k0 : kOobOffset);
-                     __builtin_amdgcn_raw_ptr_buffer_load_lds(j < kLoadsPerOp ? rx : rw, (lds_ptr_t)m0, 16, o, 0, imm,
-                                                              0);
+                     const int o = full ? goff[j] + k0 : (k0 + gcol[j] < K ? goff[j] + k0 : kOobOffset);
+                     __builtin_amdgcn_raw_ptr_buffer_load_lds(kX ? rx : rw, (lds_ptr_t)m0, 16, o, 0, imm, 0);
                  } else {
                      // per-lane offset fixed for the whole kernel, stage offset scalar
-                     __builtin_amdgcn_raw_ptr_buffer_load_lds(j < kLoadsPerOp ? rx : rw, (lds_ptr_t)m0, 16, goff[i], k0,
-                                                              imm, 0);
+                     // (the array element goes through a local: passed to the
+                     // builtin directly, it makes the host pass drop the
+                     // kernel's launch stub without a diagnostic)
+                     const int o = goff[j];
+                     __builtin_amdgcn_raw_ptr_buffer_load_lds(kX ? rx : rw, (lds_ptr_t)m0, 16, o, k0, imm, 0);
                  }
              }()),
              ...);
@@ -313,7 +310,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     // 64-byte stage.
     constexpr bool kInt8 = QT == W8A8_INT8;
     constexpr int kBlk = kInt8 ? 16 : 32;  // edge of one MFMA output block
-    constexpr int kNB = 128 / kBlk;        // blocks along each edge of the wave tile
+    constexpr int kNB = 128 / kBlk;        // blocks along the wave tile's 128 activation rows
+    constexpr int kNBn = kWN / kBlk;       // blocks along its kWN output columns (weight rows)
     constexpr int kQuads = kBlk * kBlk / 64 / 4;  // groups of 4 consecutive columns per lane and block
     constexpr int KSTEPS = BK / 64;
     static_assert(KSTEPS >= 1, "stage too small for one MFMA k-step");
@@ -324,10 +322,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     const int lrow = lane & 31, half = lane >> 5;
     const int lsw = swz(lrow);
 
-    acc_t acc[kNB][kNB];
+    acc_t acc[kNBn][kNB];  // [weight block nb][activation block mb]
     auto blk = [&](int nb, int mb) -> blk_t { return acc[nb][mb]; };
     auto set_blk = [&](int nb, int mb, blk_t c) { acc[nb][mb] = c; };
-    frag_t fa[2][kNB], fb[2][kNB];
+    frag_t fa[2][kNBn], fb[2][kNB];
 
     // int8: lane l reads row l & 15 of each 16-row block, 16-byte chunk
     // l >> 4 (the chunk XOR-swizzled by the row).  read_frags adds the lane
@@ -337,13 +335,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     const int foff = (lane & 15) * BK + (((lane >> 4) ^ swz(lane & 15)) << 4);
     auto read_frags = [&](const uint8_t *stage, int kk, frag_t *af, frag_t *bf) {
         const uint8_t *xs = stage + (wm * 128) * BK;            // X rows of this wave
-        const uint8_t *ws = stage + kOpBytes + (wn * 128) * BK;  // W rows of this wave
+        const uint8_t *ws = stage + kOpBytes + (wn * kWN) * BK;  // W rows of this wave
         if constexpr (kInt8) {
             (void)kk;
             int off = foff;
             asm volatile("" : "+v"(off));
 #pragma unroll
-            for (int b = 0; b < kNB; ++b) af[b] = *reinterpret_cast<const v4i *>(ws + b * 16 * BK + off);
+            for (int b = 0; b < kNBn; ++b) af[b] = *reinterpret_cast<const v4i *>(ws + b * 16 * BK + off);
 #pragma unroll
             for (int b = 0; b < kNB; ++b) bf[b] = *reinterpret_cast<const v4i *>(xs + b * 16 * BK + off);
         } else {
@@ -351,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
             const int off0 = lrow * BK + ((c0 ^ lsw) << 4);
             const int off1 = lrow * BK + (((c0 + 1) ^ lsw) << 4);
 #pragma unroll
-            for (int b = 0; b < 4; ++b) {
+            for (int b = 0; b < kNBn; ++b) {
                 const v4i lo = *reinterpret_cast<const v4i *>(ws + b * 32 * BK + off0);
                 const v4i hi = *reinterpret_cast<const v4i *>(ws + b * 32 * BK + off1);
                 af[b] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -365,14 +363,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         }
     };
 
-    // int8: one of the 16 fragments of a stage (0..7: weight blocks, 8..15:
-    // activation blocks) into set af / bf; `lp` is the stage's base plus this
-    // lane's offset (one address per stage, the blocks at immediate offsets).
+    // int8: one of the kNBn + kNB fragments of a stage (weight blocks first,
+    // then activation blocks) into set af / bf; `lp` is the stage's base plus
+    // this lane's offset (one address per stage, the blocks at immediate
+    // offsets).
     auto read_frag_i8 = [&](const uint8_t *lp, auto idx_c, frag_t *af, frag_t *bf) {
         constexpr int I = decltype(idx_c)::value;
         if constexpr (kInt8) {
-            if constexpr (I < 8) af[I] = *reinterpret_cast<const v4i *>(lp + kOpBytes + (wn * 128 + I * 16) * BK);
-            else bf[I - 8] = *reinterpret_cast<const v4i *>(lp + (wm * 128 + (I - 8) * 16) * BK);
+            if constexpr (I < kNBn) af[I] = *reinterpret_cast<const v4i *>(lp + kOpBytes + (wn * kWN + I * 16) * BK);
+            else bf[I - kNBn] = *reinterpret_cast<const v4i *>(lp + (wm * 128 + (I - kNBn) * 16) * BK);
         }
     };
 
@@ -396,7 +395,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     auto mfmas = [&](const frag_t *af, const frag_t *bf, auto first_c) {
         constexpr bool FIRST = decltype(first_c)::value;
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb)
+        for (int nb = 0; nb < kNBn; ++nb)
 #pragma unroll
             for (int mb = 0; mb < kNB; ++mb) {
                 if constexpr (kInt8) {
@@ -412,15 +411,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     // Interleave the memory instructions of a k-step with its MFMAs so that
     // their issue (the LDS-DMA loads especially) overlaps MFMA execution
     // instead of stalling the wave in front of the matrix pipe.
-    constexpr int kMfmas = kNB * kNB;  // MFMAs per k-step
-    constexpr int kDsPerStep = 16;     // ds_read_b128 per fragment set (both types)
-    // Where the reads and loads go among a k-step's MFMAs: e4m3 spreads both
-    // over its 16 MFMAs; int8 puts the next stage's 16 fragment reads (into
-    // the other fragment set) in the first half of its 64 short MFMAs and the
-    // refill loads in the second, so that the four waves leaving a barrier
-    // together do not queue 64 KB of reads at the LDS at once.
-    constexpr int kDsLo = 0, kDsHi = kInt8 ? kMfmas / 2 : kMfmas;
-    constexpr int kVmLo = kInt8 ? kMfmas / 2 : 0, kVmHi = kMfmas;
+    constexpr int kMfmas = kNBn * kNB;             // MFMAs per k-step
+    constexpr int kDsPerStep = 2 * (kNBn + kNB);   // ds_read_b128 per e4m3 fragment set (two per fragment)
+    // e4m3 spreads the reads and loads of a k-step over its MFMAs (int8 has
+    // its own explicit order, below)
+    constexpr int kDsLo = 0, kDsHi = kMfmas;
+    constexpr int kVmLo = 0, kVmHi = kMfmas;
     auto interleave = [&](auto nvm_c) {
         constexpr int NVM = decltype(nvm_c)::value;
         [&]<int... I>(std::integer_sequence<int, I...>) {
@@ -450,11 +446,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     // and every wave is done reading stage kt (barrier), then read the first
     // fragments of stage kt+1 and issue the last MFMAs of stage kt.
     constexpr int kParts = KSTEPS;
-    constexpr int kPerPart = kLoadsPerStage / kParts;
-    static_assert(kLoadsPerStage % kParts == 0, "loads split evenly over k-steps");
+    constexpr int kPerPart = kLoads / kParts;
+    static_assert(kLoads % kParts == 0, "loads split evenly over k-steps");
     // loads still allowed in flight when stage kt+1 must be complete: stages
     // kt+2 .. kt+NST-2 whole, and the parts of stage kt+NST-1 issued so far
-    constexpr int kPending = (NST - 3) * kLoadsPerStage + (kParts - 1) * kPerPart;
+    constexpr int kPending = (NST - 3) * kLoads + (kParts - 1) * kPerPart;
     // defer (the low-rank epilogue only, last stage of a tile): this stage's
     // refill -- the next tile's stage NST - 2 -- is issued after the epilogue
     // instead, so that its buffer can hold the low-rank operands meanwhile.
@@ -488,10 +484,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                      asm volatile("s_barrier" ::: "memory");
                      __builtin_amdgcn_sched_barrier(0);
                      if constexpr (kInt8) {
-                         // 16 groups of 4 MFMAs (block row nb = g / 2, block columns
-                         // 4 (g % 2) .. + 3) in program order, each followed by its
-                         // share of the next stage's fragment reads (into the other
-                         // set) and of the refill loads
+                         // kMfmas / 4 groups of 4 MFMAs (weight block nb = g / 2,
+                         // activation blocks 4 (g % 2) .. + 3) in program order,
+                         // each followed by its even share of the next stage's
+                         // kNBn + kNB fragment reads (into the other set) and of
+                         // the kLoads refill loads.  Spread over the MFMAs, the
+                         // reads of the four waves leaving a barrier together do
+                         // not reach the LDS at once.
+                         constexpr int kGroups = kMfmas / 4, kReads = kNBn + kNB;
                          int off = foff;
                          asm volatile("" : "+v"(off));
                          const uint8_t *lp = nxt + off;
@@ -503,19 +503,22 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                                   for (int j = 0; j < 4; ++j)
                                       mfma_i8(acc[g / 2][(g % 2) * 4 + j], fa[P][g / 2], fb[P][(g % 2) * 4 + j], first);
                                   [&]<int... R>(std::integer_sequence<int, R...>) {
-                                      (read_frag_i8(lp, std::integral_constant<int, i8_read_first(g) + R>{}, fa[P ^ 1],
-                                                    fb[P ^ 1]),
+                                      (read_frag_i8(lp,
+                                                    std::integral_constant<int, spread_first(g, kReads, kGroups) + R>{},
+                                                    fa[P ^ 1], fb[P ^ 1]),
                                        ...);
-                                  }(std::make_integer_sequence<int, i8_reads_after(g)>{});
-                                  if constexpr (i8_loads_after(g)) {
+                                  }(std::make_integer_sequence<int, spread_count(g, kReads, kGroups)>{});
+                                  [&]<int... L>(std::integer_sequence<int, L...>) {
                                       if (issue)
-                                          load_part(refill, std::integral_constant<int, i8_load_part(g)>{},
-                                                    std::integral_constant<int, kLoadsPerStage>{});
-                                  }
+                                          (load_part(refill,
+                                                     std::integral_constant<int, spread_first(g, kLoads, kGroups) + L>{},
+                                                     std::integral_constant<int, kLoads>{}),
+                                           ...);
+                                  }(std::make_integer_sequence<int, spread_count(g, kLoads, kGroups)>{});
                                   __builtin_amdgcn_sched_barrier(0);
                               }()),
                               ...);
-                         }(std::make_integer_sequence<int, 16>{});
+                         }(std::make_integer_sequence<int, kGroups>{});
                      } else {
                          if (issue)
                              load_part(refill, std::integral_constant<int, kk>{}, std::integral_constant<int, kParts>{});
@@ -564,7 +567,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
           advance_cursor()),
          ...);
     }(std::make_integer_sequence<int, NST - 1>{});
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 2) * kLoadsPerStage) : "memory");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 2) * kLoads) : "memory");
     asm volatile("s_barrier" ::: "memory");
 
     // bf16 epilogue of one tile: y = bf16(acc * sx[m] * sw (+ u . l2^T) + bias[n]).
@@ -591,8 +594,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         const int cq = 4 * (el / kBlk);    // the lane's first column within a quad group
         constexpr bool kCol = EPI == kEpiColScale;
         float tm[kNB];
-        uint2 bias2[kNB][kQuads];
-        v4f swc[kCol ? kNB : 1][kCol ? kQuads : 1];  // per-channel weight scales of the lane's quads
+        uint2 bias2[kNBn][kQuads];
+        v4f swc[kCol ? kNBn : 1][kCol ? kQuads : 1];  // per-channel weight scales of the lane's quads
         const float sw = kCol ? 1.0f : p.sw[0];
 #pragma unroll
         for (int mb = 0; mb < kNB; ++mb) {
@@ -602,7 +605,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         }
         if constexpr (kCol) {
 #pragma unroll
-            for (int nb = 0; nb < kNB; ++nb)
+            for (int nb = 0; nb < kNBn; ++nb)
 #pragma unroll
                 for (int q = 0; q < kQuads; ++q) {
                     const int n = nw + nb * kBlk + 8 * q + cq;
@@ -615,7 +618,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                 }
         }
 #pragma unroll
-        for (int nb = 0; nb < kNB; ++nb)
+        for (int nb = 0; nb < kNBn; ++nb)
 #pragma unroll
             for (int q = 0; q < kQuads; ++q) {
                 const int n = nw + nb * kBlk + 8 * q + cq;
@@ -646,7 +649,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
             // lo, [256][rp] bf16 each) and l2 of its 256 columns ([256][r],
             // r == rp); every wave fetches a quarter of each.
             {
-                const int n0 = nw - wn * 128;
+                const int n0 = nw - wn * kWN;
                 const int cols_in = min(N - n0, 256);
                 const __amdgpu_buffer_rsrc_t rw2 = __builtin_amdgcn_make_buffer_rsrc(
                     (void *)(p.l2 + (size_t)n0 * p.r), (short)0, cols_in * p.r * 2, kBufferRsrcWord3);
@@ -672,7 +675,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
 #pragma unroll
                 for (int mb = 0; mb < kNB; ++mb)
 #pragma unroll
-                    for (int nb = 0; nb < kNB; ++nb) {
+                    for (int nb = 0; nb < kNBn; ++nb) {
                         const v4i c = blk(nb, mb);
                         v4f t;
 #pragma unroll
@@ -685,13 +688,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         }
         // int8 low-rank: the l2 fragments of the wave's 8 column blocks (rows
         // n of l2, the lane's 8 of up to 32 rank columns; zero past r)
-        v8bf al2[kLrBatch ? kNB : 1];
+        v8bf al2[kLrBatch ? kNBn : 1];
         if constexpr (kLrBatch) {
             const int j0 = (el >> 4) * 8;
 #pragma unroll
-            for (int nb = 0; nb < kNB; ++nb) {
+            for (int nb = 0; nb < kNBn; ++nb) {
                 al2[nb] = v8bf{};
-                if (j0 < p.r) al2[nb] = *reinterpret_cast<const v8bf *>(lb + ((wn * 128 + nb * 16 + brow) * p.r + j0) * 2);
+                if (j0 < p.r) al2[nb] = *reinterpret_cast<const v8bf *>(lb + ((wn * kWN + nb * 16 + brow) * p.r + j0) * 2);
             }
         }
 #pragma unroll
@@ -711,11 +714,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                         ul = *reinterpret_cast<const v8bf *>(ub + half_bytes + (urow * p.rp + j0) * 2);
                     }
 #pragma unroll
-                    for (int nb = 0; nb < kNB; ++nb)
+                    for (int nb = 0; nb < kNBn; ++nb)
                         set_blk(nb, mb, __builtin_bit_cast(blk_t, __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             al2[nb], uh, __builtin_bit_cast(v4f, blk(nb, mb)), 0, 0, 0)));
 #pragma unroll
-                    for (int nb = 0; nb < kNB; ++nb)
+                    for (int nb = 0; nb < kNBn; ++nb)
                         set_blk(nb, mb, __builtin_bit_cast(blk_t, __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                             al2[nb], ul, __builtin_bit_cast(v4f, blk(nb, mb)), 0, 0, 0)));
                 }
@@ -724,7 +727,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
             for (int qb = 0; qb < kPassBlocks; ++qb) {
                 const int mb = ps * kPassBlocks + qb;
 #pragma unroll
-                for (int nb = 0; nb < kNB; ++nb) {
+                for (int nb = 0; nb < kNBn; ++nb) {
                     typedef typename std::conditional<kInt8, v4f, v16f>::type vals_t;
                     vals_t v;
                     const blk_t c = blk(nb, mb);
@@ -742,7 +745,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                         // e4m3: u . l2^T of this block from the staged rows (the
                         // interleaved form above needs more registers than this
                         // instantiation has, and was slower)
-                        const int urow = wm * 128 + mb * 32 + brow, lrow2 = wn * 128 + nb * 32 + brow;
+                        const int urow = wm * 128 + mb * 32 + brow, lrow2 = wn * kWN + nb * 32 + brow;
 #pragma unroll
                         for (int ks = 0; ks < 2; ++ks) {
                             if (ks * 16 >= p.rp) break;
@@ -774,14 +777,27 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                 }
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            // 32 rows x 16 chunks: 4 rows per wave-wide instruction
+            // 32 rows x kWN / 8 chunks, read 4 rows (16 chunk slots each) per
+            // wave-wide instruction.  A 128-wide wave tile leaves as whole
+            // 256-byte row segments (non-temporal stores); a 96-wide one as
+            // 192-byte segments, whose 128-byte lines shared with the
+            // neighbouring wave's segment take cached stores so that the L2
+            // merges the two halves (non-temporal partial lines would reach
+            // memory as partial writes).
+            constexpr int kOutChunks = kWN / 8;
 #pragma unroll
             for (int it = 0; it < 8; ++it) {
                 const int r = it * 4 + (el >> 4), c = el & 15;
+                if (kOutChunks < 16 && c >= kOutChunks) continue;
                 const v4u d = *reinterpret_cast<const v4u *>(ob + r * 256 + ((c ^ (r & 15)) << 4));
                 const int m = mw + ps * 32 + r, n = nw + c * 8;
                 uint16_t *dst = out + (size_t)m * N + n;
-                if constexpr (kIn) {
+                if constexpr (kIn && BNT != 256) {
+                    const size_t seg = ((size_t)m * N + nw) * 2, at = ((size_t)m * N + n) * 2;
+                    const size_t line = at & ~(size_t)127;
+                    if (line >= seg && line + 128 <= seg + 2 * kWN) __builtin_nontemporal_store(d, reinterpret_cast<v4u *>(dst));
+                    else *reinterpret_cast<v4u *>(dst) = d;
+                } else if constexpr (kIn) {
                     __builtin_nontemporal_store(d, reinterpret_cast<v4u *>(dst));
                 } else if (m < M) {
                     if ((N & 7) == 0 && n + 7 < N) {
@@ -798,8 +814,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     };
 
     for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-        const TileCoord tc = tile_coord(tile, tiles_m, tiles_n);
-        const int mw = tc.m0 + wm * 128, nw = tc.n0 + wn * 128;
+        const TileCoord tc = tile_coord<BNT>(tile, tiles_m, tiles_n);
+        const int mw = tc.m0 + wm * 128, nw = tc.n0 + wn * kWN;
         // Stage 0 of this tile has landed (prologue, or the last stage of the
         // previous tile waited for it).  The copies of these fragments that
         // the previous tile's last stage read are dead across its epilogue.
@@ -807,7 +823,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
 
         // Interior tiles (all rows and columns in range, N % 8 == 0) take a
         // copy of the epilogue without any bounds checks.
-        const bool interior = tc.m0 + BM <= M && tc.n0 + BN <= N && (N & 7) == 0;
+        const bool interior = tc.m0 + BM <= M && tc.n0 + BNT <= N && (N & 7) == 0;
         constexpr bool kDma = EPI != kEpiI32;
         // The first NST stages start the accumulators (kt_end >= NST).  The
         // epilogue inputs are fetched before the second-to-last stage: the
@@ -842,7 +858,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
             int32_t *out = static_cast<int32_t *>(p.out);
             const int brow = lane & (kBlk - 1), cq = 4 * (lane / kBlk);
 #pragma unroll
-            for (int nb = 0; nb < kNB; ++nb)
+            for (int nb = 0; nb < kNBn; ++nb)
 #pragma unroll
                 for (int mb = 0; mb < kNB; ++mb) {
                     const int m = mw + mb * kBlk + brow;
@@ -886,13 +902,46 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
-template <int QT, int EPI>
-void launch(const GemmArgs &a, hipStream_t stream) {
-    const int tm = (a.M + BM - 1) / BM, tn = (a.N + BN - 1) / BN;
+template <int QT, int EPI, int BNT>
+void launch_width(const GemmArgs &a, hipStream_t stream) {
+    const int tm = (a.M + BM - 1) / BM, tn = (a.N + BNT - 1) / BNT;
     const int tiles = tm * tn;
     const int grid = tiles < device_cu_count() ? tiles : device_cu_count();
-    if (a.K % (BK * NST) == 0) gemm_kernel<QT, EPI, false><<<grid, kThreads, 0, stream>>>(a, tm, tn);
-    else gemm_kernel<QT, EPI, true><<<grid, kThreads, 0, stream>>>(a, tm, tn);
+    if (a.K % (BK * NST) == 0) gemm_kernel<QT, EPI, false, BNT><<<grid, kThreads, 0, stream>>>(a, tm, tn);
+    else gemm_kernel<QT, EPI, true, BNT><<<grid, kThreads, 0, stream>>>(a, tm, tn);
+}
+
+// Time of `tiles` tiles on `cus` CUs, in rounds of full-chip tile time.  A
+// partial last round with a fraction f of the CUs busy runs at the higher
+// clock the power limit then allows and takes 0.42 + 0.58 f of a full round
+// (fitted to a half round of 256 x 256 int8 tiles at K = 12288: 0.71).
+double tile_rounds(int64_t tiles, int64_t cus) {
+    const int64_t full = tiles / cus, rem = tiles % cus;
+    return (double)full + (rem ? 0.42 + 0.58 * (double)rem / (double)cus : 0.0);
+}
+
+// Tile width for a shape (bf16 epilogue): 192-wide tiles when the product
+// spans more than one round of 256-wide tiles and they finish sooner.  A
+// 192-wide tile takes 0.85 of a 256-wide one's time (measured at M8192
+// N3072 K12288: 0.75 of the products, but 17% more operand bytes per
+// product).  E.g. M8192 N3072: 384 tiles of 256 (1.71 rounds) against 512
+// of 192 (2 x 0.85 = 1.70).
+bool use_192(int M, int N) {
+    const int64_t cus = device_cu_count(), tm = (M + BM - 1) / BM;
+    const int64_t t256 = tm * ((N + 255) / 256), t192 = tm * ((N + 191) / 192);
+    if (t256 <= cus) return false;
+    return 0.85 * tile_rounds(t192, cus) < tile_rounds(t256, cus);
+}
+
+template <int QT, int EPI>
+void launch(const GemmArgs &a, hipStream_t stream) {
+    if constexpr (EPI == kEpiBf16) {
+        if (use_192(a.M, a.N)) {
+            launch_width<QT, EPI, 192>(a, stream);
+            return;
+        }
+    }
+    launch_width<QT, EPI, 256>(a, stream);
 }
 
 }  // namespace
@@ -916,7 +965,7 @@ w8a8_status gemm_check(const void *xq, const void *wq, int64_t M, int64_t N, int
     if (M > 0 && N > 0 && (!xq || !wq || !out)) return W8A8_ERR_INVALID_ARG;
     if (K < 16 || K % 16 != 0 || K > (1 << 22)) return W8A8_ERR_SHAPE;
     if (M > (1 << 30) || N > (1 << 30)) return W8A8_ERR_SHAPE;
-    const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+    const int64_t tiles = ((M + BM - 1) / BM) * ((N + 191) / 192);  // the narrower tile's count
     if (tiles > 0x7FFFFFFF) return W8A8_ERR_SHAPE;
     if (!aligned16(xq) || !aligned16(wq) || !aligned16(out)) return W8A8_ERR_ALIGN;
     return W8A8_OK;
@@ -992,6 +1041,12 @@ extern "C" w8a8_status gguf_a8_linear(w8a8_qtype qtype, const void *xq, const fl
     a.bias = bias;
     a.out = y;
     return gemm_launch(qtype, kEpiColScale, a, stream);
+}
+
+extern "C" int w8a8_probe_gemm_tile_n(int64_t M, int64_t N) {
+    using namespace w8a8;
+    if (M < 1 || N < 1 || M > (1 << 30) || N > (1 << 30)) return 0;
+    return use_192((int)M, (int)N) ? 192 : 256;
 }
 
 extern "C" w8a8_status w8a8_gemm_i32(const int8_t *xq, const int8_t *wq, int64_t M, int64_t N, int64_t K,
