@@ -130,6 +130,21 @@ def measured_peaks(w8, torch, a_codes, b_codes):
     return round(mfma_tops, 1), round(copy_gbs, 1)
 
 
+def copy_same_bytes(torch, nbytes):
+    """Time (ms) of a plain device-to-device copy moving `nbytes` in all (half
+    read, half written), over enough buffer pairs that every launch misses
+    the 256 MB Infinity Cache, timed like the rows: the streaming rate a kernel
+    moving that many bytes can expect (short transfers do not reach the rate
+    of a long copy)."""
+    half = max(16, int(nbytes // 2) // 16 * 16)
+    sets = max(2, int(np.ceil(600e6 / (2.0 * half))))
+    bufs = [(torch.empty(half, dtype=torch.uint8, device="cuda").fill_(1),
+             torch.empty(half, dtype=torch.uint8, device="cuda")) for _ in range(sets)]
+    ms = _time_row(lambda i: bufs[i % sets][1].copy_(bufs[i % sets][0]))
+    del bufs
+    return ms
+
+
 def cpu_baseline(x_bits, w_bits, b_bits, rows, rows_all):
     """The oracle (plain C) on the same workload, scaled to TOPS of the linear:
     act-quant + int8 linear of the first `rows` rows on one thread, then of
@@ -304,6 +319,9 @@ def main():
                                       "on fragments of this step's activation and weight codes")
     act.update(measured_peak=copy_gbs, frac_of_measured_peak=round(aq_gbs / copy_gbs, 4),
                measured_peak_how="device-to-device copy of 512 MiB, read + write bytes")
+    ms_copy = copy_same_bytes(torch, aq_bytes)
+    act.update(copy_same_bytes_us=round(ms_copy * 1e3, 2), copy_same_bytes_GBs=round(aq_bytes / ms_copy / 1e6, 1),
+               frac_of_same_size_copy=round(ms_copy / ms_aq, 4))
 
     if args.calibrate_copy:
         src = torch.empty(1 << 29, dtype=torch.uint8, device="cuda").fill_(1)
@@ -516,6 +534,12 @@ def other_rows(w8, torch, workloads, args):
                                   ("GB/s", "hbm", PEAK_HBM_GBS)):
             if unit in v:
                 v.update(bound=bound, peak=peak, frac=round(v[unit] / peak, 4))
+    # each HBM row beside a plain copy of its own algorithmic bytes
+    for v in res.values():
+        if "GB/s" in v:
+            nbytes = v["GB/s"] * v["us"] * 1e3
+            ms_copy = copy_same_bytes(torch, nbytes)
+            v.update(copy_same_bytes_us=round(ms_copy * 1e3, 1), frac_of_same_size_copy=round(ms_copy * 1e3 / v["us"], 4))
     return res
 
 

@@ -128,6 +128,8 @@ w8a8_status w8a8_quant_act_rowwise(w8a8_qtype qtype, const uint16_t *x, int64_t 
  * dequantization fused into the product's epilogue:
  *   acc[m, n] = sum_k xq[m, k] * wq[n, k]   (int32 exact, or f32 for e4m3)
  *   y[m, n]   = bf16(acc[m, n] * x_scale[m] * w_scale[0] + bias[n])
+ *   (in f32: acc * f32(x_scale[m] * w_scale[0]) + bias[n] as one fused
+ *   multiply-add, rounded once to bf16, nearest even)
  *   xq [M, K] codes, x_scale f32 [M]; wq [N, K] codes, w_scale one f32;
  *   bias bf16 [N] or NULL; y bf16 [M, N].
  * Shape rules: M, N >= 0; K >= 16, K % 16 == 0 (pad K with zero codes: a zero

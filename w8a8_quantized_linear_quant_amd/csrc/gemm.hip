@@ -637,6 +637,29 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                 }
                 bias2[nb][q] = b;
             }
+        // The bias as f32, one value per output column of the lane: unpacked
+        // once per tile for int8 (4 columns per block), per use for e4m3 (16
+        // per block, too many registers to hold).
+        constexpr bool kBiasF32 = kInt8;
+        float biasf[kBiasF32 ? kNBn : 1][kBiasF32 ? 4 * kQuads : 1];
+        if constexpr (kBiasF32) {
+#pragma unroll
+            for (int nb = 0; nb < kNBn; ++nb)
+#pragma unroll
+                for (int q = 0; q < kQuads; ++q) {
+                    biasf[nb][4 * q] = bf16_bits_to_f32(bias2[nb][q].x & 0xFFFFu);
+                    biasf[nb][4 * q + 1] = bf16_bits_to_f32(bias2[nb][q].x >> 16);
+                    biasf[nb][4 * q + 2] = bf16_bits_to_f32(bias2[nb][q].y & 0xFFFFu);
+                    biasf[nb][4 * q + 3] = bf16_bits_to_f32(bias2[nb][q].y >> 16);
+                }
+        }
+        auto bias_at = [&](int nb, int e) -> float {
+            if constexpr (kBiasF32) return biasf[nb][e];
+            const uint32_t w = (e & 2) ? bias2[nb][e / 4].y : bias2[nb][e / 4].x;
+            return bf16_bits_to_f32((e & 1) ? w >> 16 : w & 0xFFFFu);
+        };
+        // plain epilogue: acc * (sx[m] sw) + bias[n] in one fused multiply-add
+        constexpr bool kFma = EPI == kEpiBf16;
         constexpr bool kLr32 = EPI == kEpiLowRank32;
         constexpr bool kLrBatch = kLr32 && kInt8;
         uint8_t *ub = buf(std::integral_constant<int, NST - 1>{});
@@ -735,7 +758,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                         v = __builtin_bit_cast(vals_t, c);
                     } else {
 #pragma unroll
-                        for (int e = 0; e < 4 * kQuads; ++e) v[e] = (float)c[e] * tm[mb];
+                        for (int e = 0; e < 4 * kQuads; ++e) {
+                            if constexpr (kFma) v[e] = __builtin_fmaf((float)c[e], tm[mb], bias_at(nb, e));
+                            else v[e] = (float)c[e] * tm[mb];
+                        }
                     }
                     if constexpr (EPI == kEpiLowRank) {
                         if constexpr (kInt8) v = low_rank_add16(p, v, nw + nb * 16, mw + mb * 16, brow, el);
@@ -763,11 +789,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                     }
 #pragma unroll
                     for (int q = 0; q < kQuads; ++q) {
-                        const uint2 bb = bias2[nb][q];
-                        const float y0 = v[4 * q] + bf16_bits_to_f32(bb.x & 0xFFFFu);
-                        const float y1 = v[4 * q + 1] + bf16_bits_to_f32(bb.x >> 16);
-                        const float y2 = v[4 * q + 2] + bf16_bits_to_f32(bb.y & 0xFFFFu);
-                        const float y3 = v[4 * q + 3] + bf16_bits_to_f32(bb.y >> 16);
+                        float y[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) y[i] = kFma ? v[4 * q + i] : v[4 * q + i] + bias_at(nb, 4 * q + i);
+                        const float y0 = y[0], y1 = y[1], y2 = y[2], y3 = y[3];
                         const int row = qb * kBlk + brow;           // row within the pass
                         const int col = nb * kBlk + 8 * q + cq;     // bf16 column within the wave tile
                         const int chunk = (col >> 3) ^ (row & 15);
