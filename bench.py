@@ -17,6 +17,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -83,11 +84,22 @@ def _time_launches(fn, iters, warmup, prefill=False):
     return e0.elapsed_time(e1) / iters
 
 
+def _code_only(text):
+    """C++ source without comments and with whitespace collapsed: a comment
+    edit leaves the hash of the kernel's code unchanged (string literals with
+    comment markers do not occur in these files)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def _kernel_hash():
+    """Hash of the GEMM's code (gemm.hip and the headers it includes from the
+    library), stored with the counter summaries in profiles/."""
     h = hashlib.sha256()
     for f in ("gemm.hip", "common.hpp", "internal.hpp"):
-        with open(os.path.join(ROOT, "w8a8_quantized_linear_quant_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "w8a8_quantized_linear_quant_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -9,10 +9,11 @@
 // this kernel's epilogue, so the int32/f32 accumulators never leave registers.
 //
 // CDNA4 design:
-//  * Persistent: one 256-thread workgroup per CU walks 256x256 output tiles,
-//    4 waves in a 2x2 grid, each wave a 128x128 sub-tile held as 4x4 blocks
-//    of 32x32 MFMA accumulators (v_mfma_i32_32x32x32_i8, or
-//    v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales for e4m3): 256
+//  * Persistent: one 256-thread workgroup per CU walks 256x256 output tiles
+//    (or 256x192 where 256-wide tiles would leave a partial last round),
+//    4 waves in a 2x2 grid, each wave a 128x128 sub-tile held as 8x8 blocks
+//    of 16x16 accumulators (v_mfma_i32_16x16x64_i8) or, for e4m3, 4x4 blocks
+//    of 32x32 (v_mfma_scale_f32_32x32x64_f8f6f4 with unit scales): 256
 //    accumulator registers per lane, one wave per SIMD.
 //  * Both operands are K-contiguous ("NT"), so every lane's MFMA fragment is
 //    a contiguous 16- or 32-byte run of one row.  The weight is the MFMA's A
@@ -27,9 +28,9 @@
 //    index so the fragment reads of consecutive rows hit distinct banks.
 //  * Tiles are numbered so that the workgroups of one XCD (hardware sends
 //    workgroup i to XCD i % 8) share operand panels in that XCD's L2.
-//  * The epilogue scales, adds the bias, packs to bf16 and stages each
-//    32-row slice of a wave's sub-tile through LDS so that it leaves as
-//    16-byte stores covering 256-byte row segments.
+//  * The epilogue scales, adds the bias (one FMA per value), packs to bf16
+//    and stages each 32-row slice of a wave's sub-tile through LDS so that it
+//    leaves as 16-byte stores covering 256-byte row segments.
 #include <type_traits>
 #include <utility>
 
