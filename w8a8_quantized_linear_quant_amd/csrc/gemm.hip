@@ -452,6 +452,42 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     // loads still allowed in flight when stage kt+1 must be complete: stages
     // kt+2 .. kt+NST-2 whole, and the parts of stage kt+NST-1 issued so far
     constexpr int kPending = (NST - 3) * kLoads + (kParts - 1) * kPerPart;
+    // Low-rank epilogue (r of 16 or 32): the tile's low-rank operands go to
+    // the two ring buffers that the tile's last stage frees (its own, whose
+    // fragments every wave read before the stage's barrier, and the one whose
+    // refill it defers): u of the tile's 256 rows (hi, then lo, [256][rp]
+    // bf16 each) and l2 of its 256 columns ([256][r], r == rp); every wave
+    // fetches a quarter of each.  Issued right after that stage's barrier, so
+    // the loads are in flight while its MFMAs run.  lr_mw / lr_nw: the tile's
+    // wave origin, set by the tile loop.
+    int lr_mw = 0, lr_nw = 0;
+    auto lowrank_dma = [&]() {
+        uint8_t *ub = buf(std::integral_constant<int, NST - 1>{});
+        uint8_t *lb = buf(std::integral_constant<int, NST - 2>{});
+        const int half_bytes = 256 * p.rp * 2;
+        {
+            const int n0 = lr_nw - wn * kWN;
+            const int cols_in = min(N - n0, 256);
+            const __amdgpu_buffer_rsrc_t rw2 = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(p.l2 + (size_t)n0 * p.r), (short)0, cols_in * p.r * 2, kBufferRsrcWord3);
+            for (int i = 0; i < p.r / 8; ++i) {
+                const int off = wave * 128 * p.r + i * 1024;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rw2, (lds_ptr_t)(lb + off), 16, off + lane * 16, 0, 0, 0);
+            }
+        }
+        const int m0 = lr_mw - wm * 128;
+        const int rows_in = min(M - m0, 256);
+        const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(p.uhi + (size_t)m0 * p.rp), (short)0, rows_in * p.rp * 2, kBufferRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(p.ulo + (size_t)m0 * p.rp), (short)0, rows_in * p.rp * 2, kBufferRsrcWord3);
+        for (int i = 0; i < p.rp / 8; ++i) {  // 128 rp bytes per wave and half, 1 KB per load
+            const int off = wave * 128 * p.rp + i * 1024;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_ptr_t)(ub + off), 16, off + lane * 16, 0, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_ptr_t)(ub + half_bytes + off), 16, off + lane * 16, 0,
+                                                     0, 0);
+        }
+    };
     // defer (the low-rank epilogue only, last stage of a tile): this stage's
     // refill -- the next tile's stage NST - 2 -- is issued after the epilogue
     // instead, so that its buffer can hold the low-rank operands meanwhile.
@@ -484,6 +520,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                      // i.e. a wait for every load in flight, prefetches included
                      asm volatile("s_barrier" ::: "memory");
                      __builtin_amdgcn_sched_barrier(0);
+                     if constexpr (kMayDefer) {
+                         if (defer) lowrank_dma();
+                         __builtin_amdgcn_sched_barrier(0);
+                     }
                      if constexpr (kInt8) {
                          // kMfmas / 4 groups of 4 MFMAs (weight block nb = g / 2,
                          // activation blocks 4 (g % 2) .. + 3) in program order,
@@ -667,33 +707,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         uint8_t *lb = buf(std::integral_constant<int, NST - 2>{});
         const int half_bytes = 256 * p.rp * 2;
         if constexpr (kLr32) {
-            // The low-rank operands of the workgroup's tile go to the two ring
-            // buffers that are free during the epilogue (the last stage's, and
-            // the one whose refill was deferred): u of its 256 rows (hi, then
-            // lo, [256][rp] bf16 each) and l2 of its 256 columns ([256][r],
-            // r == rp); every wave fetches a quarter of each.
-            {
-                const int n0 = nw - wn * kWN;
-                const int cols_in = min(N - n0, 256);
-                const __amdgpu_buffer_rsrc_t rw2 = __builtin_amdgcn_make_buffer_rsrc(
-                    (void *)(p.l2 + (size_t)n0 * p.r), (short)0, cols_in * p.r * 2, kBufferRsrcWord3);
-                for (int i = 0; i < p.r / 8; ++i) {
-                    const int off = wave * 128 * p.r + i * 1024;
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rw2, (lds_ptr_t)(lb + off), 16, off + el * 16, 0, 0, 0);
-                }
-            }
-            const int m0 = mw - wm * 128;
-            const int rows_in = min(M - m0, 256);
-            const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(p.uhi + (size_t)m0 * p.rp), (short)0, rows_in * p.rp * 2, kBufferRsrcWord3);
-            const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(p.ulo + (size_t)m0 * p.rp), (short)0, rows_in * p.rp * 2, kBufferRsrcWord3);
-            for (int i = 0; i < p.rp / 8; ++i) {  // 128 rp bytes per wave and half, 1 KB per load
-                const int off = wave * 128 * p.rp + i * 1024;
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_ptr_t)(ub + off), 16, off + el * 16, 0, 0, 0);
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_ptr_t)(ub + half_bytes + off), 16, off + el * 16, 0,
-                                                         0, 0);
-            }
+            // the tile's low-rank operands were issued at its last stage
+            // (lowrank_dma); the accumulators are scaled while they land
             if constexpr (kLrBatch) {
                 // int8: scale the accumulators in place while the operands land
 #pragma unroll
@@ -842,6 +857,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
         const TileCoord tc = tile_coord<BNT>(tile, tiles_m, tiles_n);
         const int mw = tc.m0 + wm * 128, nw = tc.n0 + wn * kWN;
+        lr_mw = mw;
+        lr_nw = nw;
         // Stage 0 of this tile has landed (prologue, or the last stage of the
         // previous tile waited for it).  The copies of these fragments that
         // the previous tile's last stage read are dead across its epilogue.
