@@ -9,6 +9,7 @@ import pytest
 
 import oracle
 import workloads
+from helpers import bf16_to_f64
 
 GOLD = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -188,3 +189,32 @@ def test_svdq_brute_force_tiny():
             low = sum(sum(xf[m, k] * l1f[j, k] for k in range(K)) * l2f[n, j] for j in range(r))
             v = acc * float(sx[m]) * float(sr) + low
             assert abs(f(y[m:m + 1, n:n + 1])[0, 0] - v) <= abs(v) * 2**-8
+
+
+def test_svdq_u_needs_more_than_one_bf16():
+    """Why U = X . L1^T reaches the bf16 MFMA as two halves: on 16 rows of the
+    SVDQuant workload (X with outlier channels, L1 and L2 N(0, 0.1), r = 32),
+    the linear with U rounded to one bf16 puts outputs outside the bf16 bound
+    |d| <= 2^-7 |ref| + 1e-3 against the oracle (U unrounded), while
+    hi = bf16(U), lo = bf16(U - hi) keeps every output inside it.  The
+    residual part, the bias and the final rounding are the oracle's own."""
+    d = workloads.svdq()
+    x = d["x"][:16]
+    rq, _, sr = oracle.quant_weight_tensorwise(oracle.INT8, d["r"])
+    y_ref, xq, sx = oracle.svdq_linear(oracle.INT8, x, rq, sr, d["l1"], d["l2"], d["bias"])
+    acc = oracle.gemm_i32(xq.view(np.int8), np.asarray(rq).view(np.int8)).astype(np.float64)
+    base = acc * sx.astype(np.float64)[:, None] * float(np.float32(sr)) + bf16_to_f64(d["bias"])[None, :]
+    u = bf16_to_f64(x) @ bf16_to_f64(d["l1"]).T
+    l2 = bf16_to_f64(d["l2"])
+    ref = bf16_to_f64(y_ref)
+
+    def outside(u_used):
+        y = bf16_to_f64(oracle.f64_to_bf16(base + u_used @ l2.T))
+        return int((np.abs(y - ref) > 2.0 ** -7 * np.abs(ref) + 1e-3).sum())
+
+    hi = bf16_to_f64(oracle.f64_to_bf16(u))
+    lo = bf16_to_f64(oracle.f64_to_bf16(u - hi))
+    assert outside(u) == 0          # the recomposition matches the oracle
+    assert outside(hi) > 1000       # one bf16: 18882 of 196608 outputs on this data
+    assert outside(hi + lo) == 0
+
