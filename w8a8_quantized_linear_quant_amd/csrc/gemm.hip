@@ -20,8 +20,10 @@
 //    operand and the activations its B operand, so each lane ends up holding
 //    four consecutive output columns of one row.
 //  * K goes HBM -> LDS in BK-byte stages through a ring of NST buffers with
-//    buffer_load_dwordx4 ... lds (no register staging); the ring runs NST - 1
-//    stages ahead, across tile boundaries.  Buffer loads past num_records
+//    buffer_load_dwordx4 ... lds (no register staging): int8 128-byte stages
+//    in a ring of two (every load instruction reads whole 128-byte lines),
+//    e4m3 64-byte stages in a ring of four.  The ring runs ahead across tile
+//    boundaries.  Buffer loads past num_records
 //    read zero, which covers ragged M/N tails and (with an out-of-range
 //    offset) the ragged K tail.
 //  * Within a stage, 16-byte chunks of each row are XOR-swizzled by the row
@@ -50,25 +52,33 @@ constexpr int kThreads = 256;
 constexpr int kGroupM = W8A8_GEMM_GROUP_M;  // tile-ordering group height
 constexpr int kXcds = 8;
 
-#ifndef W8A8_GEMM_BK
-#define W8A8_GEMM_BK 64  // bytes of K per LDS stage
-#endif
-#ifndef W8A8_GEMM_NST
-#define W8A8_GEMM_NST 4  // LDS stages (loads run NST - 1 stages ahead)
-#endif
-constexpr int BK = W8A8_GEMM_BK;
-constexpr int NST = W8A8_GEMM_NST;
-constexpr int kOpBytes = 256 * BK;         // one operand tile per stage
-constexpr int kStageBytes = 2 * kOpBytes;  // X tile then W tile
-constexpr int kChunks = BK / 16;           // 16-byte chunks per row
-constexpr int kRowsPerLoad = 64 / kChunks; // rows one wave-wide 1 KB load covers
-constexpr int kLoadsPerOp = 64 / kRowsPerLoad;  // per wave and operand: 64 rows (of 256)
-constexpr int kLoadsPerStage = 2 * kLoadsPerOp; // the most a stage issues per wave (256-wide tile)
-constexpr int kImmLoads = kLoadsPerOp < 4 ? kLoadsPerOp : 4;  // loads per M0 value (immediate offsets < 4 KB)
 constexpr int kOutWaveBytes = 32 * 256;    // epilogue staging per wave
-static_assert(NST >= 3 && NST <= 4, "3..4 LDS stages");
-static_assert(NST * kStageBytes + 4 * kOutWaveBytes <= 160 * 1024, "LDS budget");
-static_assert((NST - 1) * kLoadsPerStage <= 63, "vmcnt range");
+constexpr int kMaxRpStaged = 32;           // largest rank whose low-rank operands are staged in LDS
+
+// Stage geometry: BK bytes of K per LDS stage, a ring of NST stage buffers.
+// int8 takes 128-byte stages in a ring of two: each LDS-DMA instruction then
+// reads 8 rows x one whole 128-byte line, where 64-byte stages read 16 rows x
+// half a line; the vector memory path moves the same bytes ~7% faster as
+// whole lines (M4096 N12288 K3072: 112.3 vs 121.2 us per launch).  e4m3
+// keeps 64-byte stages in a ring of four, which measured faster for it
+// (257.5 vs 263.7 us at M8192 N12288 K3072).
+template <int BK_, int NST_>
+struct StageGeo {
+    static constexpr int BK = BK_;
+    static constexpr int NST = NST_;
+    static constexpr int kOpBytes = 256 * BK;          // one operand tile per stage
+    static constexpr int kStageBytes = 2 * kOpBytes;   // X tile then W tile
+    static constexpr int kChunks = BK / 16;            // 16-byte chunks per row
+    static constexpr int kRowsPerLoad = 64 / kChunks;  // rows one wave-wide 1 KB load covers
+    static constexpr int kLoadsPerOp = 64 / kRowsPerLoad;   // per wave and operand: 64 rows (of 256)
+    static constexpr int kLoadsPerStage = 2 * kLoadsPerOp;  // the most a stage issues per wave
+    static constexpr int kImmLoads = kLoadsPerOp < 4 ? kLoadsPerOp : 4;  // loads per M0 value (imm < 4 KB)
+    static_assert(NST >= 2 && NST <= 4, "2..4 LDS stages");
+    static_assert(NST * kStageBytes + 4 * kOutWaveBytes <= 160 * 1024, "LDS budget");
+    static_assert((NST - 1) * kLoadsPerStage <= 63, "vmcnt range");
+};
+template <int QT>
+using Geo = typename std::conditional<QT == W8A8_INT8, StageGeo<128, 2>, StageGeo<64, 4>>::type;
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
@@ -84,6 +94,7 @@ constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 // reads of 16 consecutive rows (same logical chunk) spread over distinct bank
 // groups whether the LDS serves 8 or 16 lanes of a 128-bit read per cycle.
 // It depends on row % 16 only, so it is the same for every 32-row block.
+template <int kChunks>
 __device__ __forceinline__ int swz(int row) {
     if constexpr (kChunks == 8) return (row & 7) ^ ((row >> 3) & 1);
     else return ((row >> 1) ^ (row >> 2)) & 3;
@@ -183,6 +194,12 @@ __device__ __forceinline__ v4f low_rank_add16(const GemmArgs &p, v4f v, int nbas
 template <int QT, int EPI, bool TAIL, int BNT>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m, int tiles_n) {
     static_assert(BNT == 256 || (BNT == 192 && EPI == kEpiBf16), "192-wide tiles: bf16 epilogue only");
+    using G = Geo<QT>;
+    constexpr int BK = G::BK, NST = G::NST, kOpBytes = G::kOpBytes, kStageBytes = G::kStageBytes;
+    constexpr int kChunks = G::kChunks, kRowsPerLoad = G::kRowsPerLoad, kLoadsPerOp = G::kLoadsPerOp;
+    constexpr int kImmLoads = G::kImmLoads;
+    static_assert(EPI != kEpiLowRank32 || NST != 2 || kStageBytes >= 3 * 256 * kMaxRpStaged * 2,
+                  "two-stage ring: u and l2 share the last stage's buffer");
     constexpr int kWN = BNT / 2;                 // wave tile width along N
     constexpr int kRowsW = BNT / 4;              // weight rows each wave loads per stage
     constexpr int kLoadsW = kRowsW / kRowsPerLoad;
@@ -228,7 +245,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     for (int j = 0; j < kLoads; ++j) {
         const int i = j < kLoadsPerOp ? j : j - kLoadsPerOp;
         const int row = (j < kLoadsPerOp ? wave * 64 : wave * kRowsW) + i * kRowsPerLoad + lane / kChunks;
-        const int c = (lane % kChunks) ^ swz(row);
+        const int c = (lane % kChunks) ^ swz<kChunks>(row);
         gcol[j] = c * 16;
         // the instruction's immediate offset (i KB, see load_part) is added to
         // the global address as well as to the LDS address; take it back out
@@ -316,12 +333,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     constexpr int kQuads = kBlk * kBlk / 64 / 4;  // groups of 4 consecutive columns per lane and block
     constexpr int KSTEPS = BK / 64;
     static_assert(KSTEPS >= 1, "stage too small for one MFMA k-step");
-    static_assert(!kInt8 || BK == 64, "int8 fragment offsets assume one k-step of 64 bytes per stage");
+    static_assert(!kInt8 || KSTEPS == 1 || NST == 2, "int8 with several k-steps per stage: two-stage ring only");
     typedef typename std::conditional<kInt8, v4i, v8i>::type frag_t;
     typedef typename std::conditional<kInt8, v4i, v16f>::type acc_t;  // one block's accumulators
     typedef acc_t blk_t;
     const int lrow = lane & 31, half = lane >> 5;
-    const int lsw = swz(lrow);
+    const int lsw = swz<kChunks>(lrow);
 
     acc_t acc[kNBn][kNB];  // [weight block nb][activation block mb]
     auto blk = [&](int nb, int mb) -> blk_t { return acc[nb][mb]; };
@@ -333,13 +350,12 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     // offset to the stage's base through an opaque copy, so the compiler
     // does not keep a precomputed address per stage buffer alive across the
     // loop.
-    const int foff = (lane & 15) * BK + (((lane >> 4) ^ swz(lane & 15)) << 4);
+    auto foff = [&](int kk) { return (lane & 15) * BK + (((kk * 4 + (lane >> 4)) ^ swz<kChunks>(lane & 15)) << 4); };
     auto read_frags = [&](const uint8_t *stage, int kk, frag_t *af, frag_t *bf) {
         const uint8_t *xs = stage + (wm * 128) * BK;            // X rows of this wave
         const uint8_t *ws = stage + kOpBytes + (wn * kWN) * BK;  // W rows of this wave
         if constexpr (kInt8) {
-            (void)kk;
-            int off = foff;
+            int off = foff(kk);
             asm volatile("" : "+v"(off));
 #pragma unroll
             for (int b = 0; b < kNBn; ++b) af[b] = *reinterpret_cast<const v4i *>(ws + b * 16 * BK + off);
@@ -446,12 +462,29 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     // step kk run.  Before the last k-step: wait until stage kt+1 has landed
     // and every wave is done reading stage kt (barrier), then read the first
     // fragments of stage kt+1 and issue the last MFMAs of stage kt.
+    // Two-stage ring (NST == 2): a stage's buffer is free only after the
+    // barrier of its last k-step, so the whole refill (the stage two ahead,
+    // into the buffer just freed) is issued in that k-step, and the wait at
+    // the end of the next stage is for everything in flight.
     constexpr int kParts = KSTEPS;
     constexpr int kPerPart = kLoads / kParts;
     static_assert(kLoads % kParts == 0, "loads split evenly over k-steps");
+    constexpr int kLoadsEarly = NST == 2 ? 0 : kPerPart;   // loads per k-step before the last
+    constexpr int kLoadsLast = NST == 2 ? kLoads : kPerPart;  // loads in the last k-step
     // loads still allowed in flight when stage kt+1 must be complete: stages
     // kt+2 .. kt+NST-2 whole, and the parts of stage kt+NST-1 issued so far
-    constexpr int kPending = (NST - 3) * kLoads + (kParts - 1) * kPerPart;
+    constexpr int kPending = NST == 2 ? 0 : (NST - 3) * kLoads + (kParts - 1) * kPerPart;
+    constexpr int kPendingDeferred = NST == 2 ? 0 : kPending - (kParts - 1) * kPerPart;
+    // Buffers of the low-rank operands: u (hi, then lo) in the tile's last
+    // stage's buffer, l2 in the buffer whose refill that stage defers (with
+    // two stages the same 64 KB buffer, l2 after u's 32 KB).
+    auto lr_ubuf = [&]() { return buf(std::integral_constant<int, NST - 1>{}); };
+    auto lr_lbuf = [&]() {
+        if constexpr (NST == 2) return buf(std::integral_constant<int, 1>{}) + 2 * 256 * kMaxRpStaged * 2;
+        else return buf(std::integral_constant<int, NST - 2>{});
+    };
+    // buffer of the refill a tile's last stage defers (low-rank epilogue)
+    constexpr int kDeferBuf = NST == 2 ? 1 : NST - 2;
     // Low-rank epilogue (r of 16 or 32): the tile's low-rank operands go to
     // the two ring buffers that the tile's last stage frees (its own, whose
     // fragments every wave read before the stage's barrier, and the one whose
@@ -462,8 +495,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     // wave origin, set by the tile loop.
     int lr_mw = 0, lr_nw = 0;
     auto lowrank_dma = [&]() {
-        uint8_t *ub = buf(std::integral_constant<int, NST - 1>{});
-        uint8_t *lb = buf(std::integral_constant<int, NST - 2>{});
+        uint8_t *ub = lr_ubuf();
+        uint8_t *lb = lr_lbuf();
         const int half_bytes = 256 * p.rp * 2;
         {
             const int n0 = lr_nw - wn * kWN;
@@ -498,23 +531,18 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         const bool issue = !kMayDefer || !defer;
         uint8_t *cur = buf(sc);
         uint8_t *nxt = buf(std::integral_constant<int, (S + 1) % NST>{});
-        uint8_t *refill = buf(std::integral_constant<int, (S + NST - 1) % NST>{});
+        // NST >= 3: the buffer stage S - 1 used; two stages: this stage's own
+        // (free after its last k-step's barrier)
+        uint8_t *refill = buf(std::integral_constant<int, NST == 2 ? S : (S + NST - 1) % NST>{});
         [&]<int... KK>(std::integer_sequence<int, KK...>) {
             (([&] {
                  constexpr int kk = KK;
                  constexpr int P = (S * KSTEPS + kk) & 1;
-                 if constexpr (kk + 1 < KSTEPS) {
-                     __builtin_amdgcn_sched_barrier(0);
-                     read_frags(cur, kk + 1, fa[P ^ 1], fb[P ^ 1]);
-                     if (issue)
-                         load_part(refill, std::integral_constant<int, kk>{}, std::integral_constant<int, kParts>{});
-                     mfmas(fa[P], fb[P], std::integral_constant<bool, FIRST && S == 0 && kk == 0>{});
-                     interleave(std::integral_constant<int, kPerPart>{});
-                     __builtin_amdgcn_sched_barrier(0);
-                 } else {
+                 constexpr bool kLast = kk + 1 == KSTEPS;
+                 if constexpr (kLast) {
                      // without this stage's earlier parts in flight, fewer may remain
                      if (issue) __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPending));
-                     else __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPending - (kParts - 1) * kPerPart));
+                     else __builtin_amdgcn_s_waitcnt(waitcnt_vm(kPendingDeferred));
                      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
                      // a bare barrier: __syncthreads() would add a release fence,
                      // i.e. a wait for every load in flight, prefetches included
@@ -524,50 +552,67 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                          if (defer) lowrank_dma();
                          __builtin_amdgcn_sched_barrier(0);
                      }
-                     if constexpr (kInt8) {
-                         // kMfmas / 4 groups of 4 MFMAs (weight block nb = g / 2,
-                         // activation blocks 4 (g % 2) .. + 3) in program order,
-                         // each followed by its even share of the next stage's
-                         // kNBn + kNB fragment reads (into the other set) and of
-                         // the kLoads refill loads.  Spread over the MFMAs, the
-                         // reads of the four waves leaving a barrier together do
-                         // not reach the LDS at once.
-                         constexpr int kGroups = kMfmas / 4, kReads = kNBn + kNB;
-                         int off = foff;
-                         asm volatile("" : "+v"(off));
-                         const uint8_t *lp = nxt + off;
-                         [&]<int... G>(std::integer_sequence<int, G...>) {
-                             (([&] {
-                                  constexpr int g = G;
-                                  constexpr auto first = std::integral_constant<bool, FIRST && S == 0>{};
+                 } else {
+                     __builtin_amdgcn_sched_barrier(0);
+                 }
+                 if constexpr (kInt8) {
+                     // kMfmas / 4 groups of 4 MFMAs (weight block nb = g / 2,
+                     // activation blocks 4 (g % 2) .. + 3) in program order,
+                     // each followed by its even share of the next k-step's
+                     // kNBn + kNB fragment reads (into the other set; the next
+                     // stage's first k-step after the barrier) and of the
+                     // k-step's refill loads.  Spread over the MFMAs, the
+                     // reads of the four waves leaving a barrier together do
+                     // not reach the LDS at once.
+                     constexpr int kGroups = kMfmas / 4, kReads = kNBn + kNB;
+                     constexpr int kL = kLast ? kLoadsLast : kLoadsEarly;
+                     constexpr int kPart0 = kLast ? 0 : kk;  // first load part of this k-step, in units of kL
+                     int off = foff(kLast ? 0 : kk + 1);
+                     asm volatile("" : "+v"(off));
+                     const uint8_t *lp = (kLast ? nxt : cur) + off;
+                     [&]<int... G>(std::integer_sequence<int, G...>) {
+                         (([&] {
+                              constexpr int g = G;
+                              constexpr auto first = std::integral_constant<bool, FIRST && S == 0 && kk == 0>{};
 #pragma unroll
-                                  for (int j = 0; j < 4; ++j)
-                                      mfma_i8(acc[g / 2][(g % 2) * 4 + j], fa[P][g / 2], fb[P][(g % 2) * 4 + j], first);
-                                  [&]<int... R>(std::integer_sequence<int, R...>) {
-                                      (read_frag_i8(lp,
-                                                    std::integral_constant<int, spread_first(g, kReads, kGroups) + R>{},
-                                                    fa[P ^ 1], fb[P ^ 1]),
+                              for (int j = 0; j < 4; ++j)
+                                  mfma_i8(acc[g / 2][(g % 2) * 4 + j], fa[P][g / 2], fb[P][(g % 2) * 4 + j], first);
+                              [&]<int... R>(std::integer_sequence<int, R...>) {
+                                  (read_frag_i8(lp, std::integral_constant<int, spread_first(g, kReads, kGroups) + R>{},
+                                                fa[P ^ 1], fb[P ^ 1]),
+                                   ...);
+                              }(std::make_integer_sequence<int, spread_count(g, kReads, kGroups)>{});
+                              [&]<int... L>(std::integer_sequence<int, L...>) {
+                                  if (issue)
+                                      (load_part(refill,
+                                                 std::integral_constant<int, kPart0 * kL + spread_first(g, kL, kGroups) + L>{},
+                                                 std::integral_constant<int, kLoads>{}),
                                        ...);
-                                  }(std::make_integer_sequence<int, spread_count(g, kReads, kGroups)>{});
-                                  [&]<int... L>(std::integer_sequence<int, L...>) {
-                                      if (issue)
-                                          (load_part(refill,
-                                                     std::integral_constant<int, spread_first(g, kLoads, kGroups) + L>{},
-                                                     std::integral_constant<int, kLoads>{}),
-                                           ...);
-                                  }(std::make_integer_sequence<int, spread_count(g, kLoads, kGroups)>{});
-                                  __builtin_amdgcn_sched_barrier(0);
-                              }()),
-                              ...);
-                         }(std::make_integer_sequence<int, kGroups>{});
-                     } else {
+                              }(std::make_integer_sequence<int, spread_count(g, kL, kGroups)>{});
+                              __builtin_amdgcn_sched_barrier(0);
+                          }()),
+                          ...);
+                     }(std::make_integer_sequence<int, kGroups>{});
+                 } else if constexpr (!kLast) {
+                     read_frags(cur, kk + 1, fa[P ^ 1], fb[P ^ 1]);
+                     if constexpr (kLoadsEarly > 0) {
                          if (issue)
                              load_part(refill, std::integral_constant<int, kk>{}, std::integral_constant<int, kParts>{});
-                         read_frags(nxt, 0, fa[P ^ 1], fb[P ^ 1]);
-                         mfmas(fa[P], fb[P], std::integral_constant<bool, FIRST && S == 0 && kk == 0>{});
-                         interleave(std::integral_constant<int, kPerPart>{});
-                         __builtin_amdgcn_sched_barrier(0);
                      }
+                     mfmas(fa[P], fb[P], std::integral_constant<bool, FIRST && S == 0 && kk == 0>{});
+                     interleave(std::integral_constant<int, kLoadsEarly>{});
+                     __builtin_amdgcn_sched_barrier(0);
+                 } else {
+                     if (issue) {
+                         if constexpr (NST == 2)
+                             load_part(refill, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
+                         else
+                             load_part(refill, std::integral_constant<int, kk>{}, std::integral_constant<int, kParts>{});
+                     }
+                     read_frags(nxt, 0, fa[P ^ 1], fb[P ^ 1]);
+                     mfmas(fa[P], fb[P], std::integral_constant<bool, FIRST && S == 0 && kk == 0>{});
+                     interleave(std::integral_constant<int, kLoadsLast>{});
+                     __builtin_amdgcn_sched_barrier(0);
                  }
              }()),
              ...);
@@ -601,14 +646,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         }
     };
 
-    // Prologue: stages 0 .. NST-2 in flight, wait for stage 0.
+    // Prologue: stages 0 .. NST-2 in flight (0 and 1 with two stages), wait
+    // for stage 0.
+    constexpr int kPro = NST == 2 ? 2 : NST - 1;
     [&]<int... S>(std::integer_sequence<int, S...>) {
         ((load_part(buf(std::integral_constant<int, S>{}), std::integral_constant<int, 0>{},
                     std::integral_constant<int, 1>{}),
           advance_cursor()),
          ...);
-    }(std::make_integer_sequence<int, NST - 1>{});
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((NST - 2) * kLoads) : "memory");
+    }(std::make_integer_sequence<int, kPro>{});
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"((kPro - 1) * kLoads) : "memory");
     asm volatile("s_barrier" ::: "memory");
 
     // bf16 epilogue of one tile: y = bf16(acc * sx[m] * sw (+ u . l2^T) + bias[n]).
@@ -703,8 +750,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         constexpr bool kFma = EPI == kEpiBf16;
         constexpr bool kLr32 = EPI == kEpiLowRank32;
         constexpr bool kLrBatch = kLr32 && kInt8;
-        uint8_t *ub = buf(std::integral_constant<int, NST - 1>{});
-        uint8_t *lb = buf(std::integral_constant<int, NST - 2>{});
+        uint8_t *ub = lr_ubuf();
+        uint8_t *lb = lr_lbuf();
         const int half_bytes = 256 * p.rp * 2;
         if constexpr (kLr32) {
             // the tile's low-rank operands were issued at its last stage
@@ -930,9 +977,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         if constexpr (EPI == kEpiLowRank32) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             asm volatile("s_barrier" ::: "memory");
-            // the refill deferred from the tile's last stage: the next tile's
-            // stage NST - 2, into the buffer that held l2
-            load_part(buf(std::integral_constant<int, NST - 2>{}), std::integral_constant<int, 0>{},
+            // the refill deferred from the tile's last stage (the next tile's
+            // stage NST - 2, or stage 1 with two stages), into the buffer
+            // that held l2
+            load_part(buf(std::integral_constant<int, kDeferBuf>{}), std::integral_constant<int, 0>{},
                       std::integral_constant<int, 1>{});
             advance_cursor();
         }
@@ -950,7 +998,7 @@ void launch_width(const GemmArgs &a, hipStream_t stream) {
     const int tm = (a.M + BM - 1) / BM, tn = (a.N + BNT - 1) / BNT;
     const int tiles = tm * tn;
     const int grid = tiles < device_cu_count() ? tiles : device_cu_count();
-    if (a.K % (BK * NST) == 0) gemm_kernel<QT, EPI, false, BNT><<<grid, kThreads, 0, stream>>>(a, tm, tn);
+    if (a.K % (Geo<QT>::BK * Geo<QT>::NST) == 0) gemm_kernel<QT, EPI, false, BNT><<<grid, kThreads, 0, stream>>>(a, tm, tn);
     else gemm_kernel<QT, EPI, true, BNT><<<grid, kThreads, 0, stream>>>(a, tm, tn);
 }
 
