@@ -78,7 +78,7 @@ struct StageGeo {
     static_assert((NST - 1) * kLoadsPerStage <= 63, "vmcnt range");
 };
 template <int QT>
-using Geo = typename std::conditional<QT == W8A8_INT8, StageGeo<128, 2>, StageGeo<64, 4>>::type;
+using Geo = StageGeo<128, 2>;
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
@@ -392,6 +392,23 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         }
     };
 
+    // e4m3: half I % 2 of fragment I / 2 of a k-step (weight blocks first,
+    // then activation blocks), 16 of the fragment's 32 bytes, into set af / bf.
+    // lp0 / lp1: the stage's base plus this lane's offset of either half.
+    auto read_half_f8 = [&](const uint8_t *lp0, const uint8_t *lp1, auto idx_c, frag_t *af, frag_t *bf) {
+        constexpr int I = decltype(idx_c)::value;
+        if constexpr (!kInt8) {
+            constexpr int f = I / 2, h = I % 2;
+            const uint8_t *lp = h ? lp1 : lp0;
+            v4i v;
+            if constexpr (f < kNBn) v = *reinterpret_cast<const v4i *>(lp + kOpBytes + (wn * kWN + f * 32) * BK);
+            else v = *reinterpret_cast<const v4i *>(lp + (wm * 128 + (f - kNBn) * 32) * BK);
+            frag_t &dst = f < kNBn ? af[f < kNBn ? f : 0] : bf[f < kNBn ? 0 : f - kNBn];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dst[4 * h + e] = v[e];
+        }
+    };
+
     // FIRST: the tile's first k-step, which starts the accumulators from an
     // inline-constant zero instead of zeroing 256 registers beforehand.
     // One int8 MFMA, accumulator tied to its AGPRs.  Written as inline asm:
@@ -409,46 +426,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         else
             asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
     };
-    auto mfmas = [&](const frag_t *af, const frag_t *bf, auto first_c) {
-        constexpr bool FIRST = decltype(first_c)::value;
-#pragma unroll
-        for (int nb = 0; nb < kNBn; ++nb)
-#pragma unroll
-            for (int mb = 0; mb < kNB; ++mb) {
-                if constexpr (kInt8) {
-                    mfma_i8(acc[nb][mb], af[nb], bf[mb], std::integral_constant<bool, FIRST>{});
-                } else {
-                    const acc_t c = FIRST ? acc_t{} : acc[nb][mb];
-                    acc[nb][mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[nb], bf[mb], c, 0, 0, 0, 127, 0,
-                                                                                  127);
-                }
-            }
+    // One e4m3 MFMA with unit block scales (E8M0 127 = 2^0), written as inline
+    // asm for the same reason and tied the same way: as a builtin the
+    // scheduler moved the MFMAs past the explicit order of the K loop (even
+    // above the stage barrier) and issued a k-step's MFMAs back to back.
+    const int scale_one = 127;
+    auto mfma_f8 = [&](v16f &c, const v8i &a, const v8i &b, auto first_c) {
+        if constexpr (decltype(first_c)::value)
+            asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, 0, %3, %3 op_sel_hi:[0,0,0]"
+                         : "=a"(c)
+                         : "v"(a), "v"(b), "v"(scale_one));
+        else
+            asm volatile("v_mfma_scale_f32_32x32x64_f8f6f4 %0, %1, %2, %0, %3, %3 op_sel_hi:[0,0,0]"
+                         : "+a"(c)
+                         : "v"(a), "v"(b), "v"(scale_one));
     };
-
-    // Interleave the memory instructions of a k-step with its MFMAs so that
-    // their issue (the LDS-DMA loads especially) overlaps MFMA execution
-    // instead of stalling the wave in front of the matrix pipe.
-    constexpr int kMfmas = kNBn * kNB;             // MFMAs per k-step
-    constexpr int kDsPerStep = 2 * (kNBn + kNB);   // ds_read_b128 per e4m3 fragment set (two per fragment)
-    // e4m3 spreads the reads and loads of a k-step over its MFMAs (int8 has
-    // its own explicit order, below)
-    constexpr int kDsLo = 0, kDsHi = kMfmas;
-    constexpr int kVmLo = 0, kVmHi = kMfmas;
-    auto interleave = [&](auto nvm_c) {
-        constexpr int NVM = decltype(nvm_c)::value;
-        [&]<int... I>(std::integer_sequence<int, I...>) {
-            (([&] {
-                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-                 constexpr int di = I - kDsLo, dn = kDsHi - kDsLo;
-                 constexpr int ds = (I >= kDsLo && I < kDsHi) ? (di + 1) * kDsPerStep / dn - di * kDsPerStep / dn : 0;
-                 if constexpr (ds > 0) __builtin_amdgcn_sched_group_barrier(0x100, ds, 0);  // DS reads
-                 constexpr int vi = I - kVmLo, vn = kVmHi - kVmLo;
-                 constexpr int vm = (I >= kVmLo && I < kVmHi) ? (vi + 1) * NVM / vn - vi * NVM / vn : 0;
-                 if constexpr (vm > 0) __builtin_amdgcn_sched_group_barrier(0x020, vm, 0);  // VMEM reads
-             }()),
-             ...);
-        }(std::make_integer_sequence<int, kMfmas>{});
-    };
+    // MFMAs per k-step.  Each k-step's memory instructions are placed among
+    // its MFMAs in an explicit program order (run_stage) so that their issue
+    // (the LDS-DMA loads especially) overlaps MFMA execution instead of
+    // stalling the wave in front of the matrix pipe.
+    constexpr int kMfmas = kNBn * kNB;
 
     // Within a stage the fragments of k-step kk+1 are read while the MFMAs of
     // step kk run.  At the last step of a stage: wait until the next stage
@@ -593,26 +590,50 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                           }()),
                           ...);
                      }(std::make_integer_sequence<int, kGroups>{});
-                 } else if constexpr (!kLast) {
-                     read_frags(cur, kk + 1, fa[P ^ 1], fb[P ^ 1]);
-                     if constexpr (kLoadsEarly > 0) {
-                         if (issue)
-                             load_part(refill, std::integral_constant<int, kk>{}, std::integral_constant<int, kParts>{});
-                     }
-                     mfmas(fa[P], fb[P], std::integral_constant<bool, FIRST && S == 0 && kk == 0>{});
-                     interleave(std::integral_constant<int, kLoadsEarly>{});
-                     __builtin_amdgcn_sched_barrier(0);
                  } else {
-                     if (issue) {
-                         if constexpr (NST == 2)
-                             load_part(refill, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
-                         else
-                             load_part(refill, std::integral_constant<int, kk>{}, std::integral_constant<int, kParts>{});
-                     }
-                     read_frags(nxt, 0, fa[P ^ 1], fb[P ^ 1]);
-                     mfmas(fa[P], fb[P], std::integral_constant<bool, FIRST && S == 0 && kk == 0>{});
-                     interleave(std::integral_constant<int, kLoadsLast>{});
-                     __builtin_amdgcn_sched_barrier(0);
+                     // e4m3: the same explicit order with one MFMA per group
+                     // (kMfmas 32x32x64 MFMAs per k-step) and the next k-step's
+                     // fragments read as 16-byte halves.  Left to
+                     // sched_group_barrier hints, the compiler issued a
+                     // k-step's MFMAs back to back and every read and load
+                     // after them, so the next k-step's first MFMA waited for
+                     // the LDS.
+                     constexpr int kGroups = kMfmas, kReads = 2 * (kNBn + kNB);
+                     constexpr int kL = kLast ? kLoadsLast : kLoadsEarly;
+                     constexpr int kPart0 = kLast ? 0 : kk;
+                     constexpr int kNext = kLast ? 0 : kk + 1;
+                     // the lane's offsets of the two halves, opaque to the
+                     // compiler: with addresses it could trace to one stage
+                     // buffer, it made some reads wait for this k-step's
+                     // LDS-DMA loads into the other (vmcnt(0))
+                     int off0 = lrow * BK + (((kNext * 4 + half * 2) ^ lsw) << 4);
+                     int off1 = lrow * BK + (((kNext * 4 + half * 2 + 1) ^ lsw) << 4);
+                     asm volatile("" : "+v"(off0), "+v"(off1));
+                     const uint8_t *src = kLast ? nxt : cur;
+                     const uint8_t *lp0 = src + off0, *lp1 = src + off1;
+                     [&]<int... G>(std::integer_sequence<int, G...>) {
+                         (([&] {
+                              constexpr int g = G;
+                              constexpr int nb = g / kNB, mb = g % kNB;
+                              constexpr auto first = std::integral_constant<bool, FIRST && S == 0 && kk == 0>{};
+                              if constexpr (!kInt8) mfma_f8(acc[nb][mb], fa[P][nb], fb[P][mb], first);
+                              [&]<int... R>(std::integer_sequence<int, R...>) {
+                                  (read_half_f8(lp0, lp1,
+                                                std::integral_constant<int, spread_first(g, kReads, kGroups) + R>{},
+                                                fa[P ^ 1], fb[P ^ 1]),
+                                   ...);
+                              }(std::make_integer_sequence<int, spread_count(g, kReads, kGroups)>{});
+                              [&]<int... L>(std::integer_sequence<int, L...>) {
+                                  if (issue)
+                                      (load_part(refill,
+                                                 std::integral_constant<int, kPart0 * kL + spread_first(g, kL, kGroups) + L>{},
+                                                 std::integral_constant<int, kLoads>{}),
+                                       ...);
+                              }(std::make_integer_sequence<int, spread_count(g, kL, kGroups)>{});
+                              __builtin_amdgcn_sched_barrier(0);
+                          }()),
+                          ...);
+                     }(std::make_integer_sequence<int, kGroups>{});
                  }
              }()),
              ...);
@@ -937,11 +958,13 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         }
 
         // --------------------------------------------------------- epilogue
-        // int8: the last MFMAs were inline asm, which the compiler's hazard
-        // tracking does not see; give their results the wait states an MFMA
-        // result needs before other instructions read it (24 >= the 16x16x64
-        // requirement) before the epilogue touches the accumulators.
+        // The last MFMAs were inline asm, which the compiler's hazard tracking
+        // does not see; give their results the wait states an MFMA result
+        // needs before other instructions read it (24 >= the 16x16x64 int8
+        // requirement, 32 >= the 16-pass 32x32x64 e4m3 one) before the
+        // epilogue touches the accumulators.
         if constexpr (kInt8) asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+        else asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
         // Block (nb, mb), register 4j+i holds output row m = mbase + (l & 31)
         // and column n = nbase + 8j + 4(l >> 5) + i.
         if constexpr (EPI == kEpiI32) {
