@@ -776,20 +776,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         const int half_bytes = 256 * p.rp * 2;
         if constexpr (kLr32) {
             // the tile's low-rank operands were issued at its last stage
-            // (lowrank_dma); the accumulators are scaled while they land
-            if constexpr (kLrBatch) {
-                // int8: scale the accumulators in place while the operands land
-#pragma unroll
-                for (int mb = 0; mb < kNB; ++mb)
-#pragma unroll
-                    for (int nb = 0; nb < kNBn; ++nb) {
-                        const v4i c = blk(nb, mb);
-                        v4f t;
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) t[e] = (float)c[e] * tm[mb];
-                        set_blk(nb, mb, __builtin_bit_cast(blk_t, t));
-                    }
-            }
+            // (lowrank_dma)
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             asm volatile("s_barrier" ::: "memory");
         }
@@ -804,12 +791,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                 if (j0 < p.r) al2[nb] = *reinterpret_cast<const v8bf *>(lb + ((wn * kWN + nb * 16 + brow) * p.r + j0) * 2);
             }
         }
+        // int8 low-rank: one pass's 16 blocks, dequantized with their bias
+        // and then given u . l2^T
+        v4f lrv[kLrBatch ? kPassBlocks : 1][kLrBatch ? kNBn : 1];
 #pragma unroll
         for (int ps = 0; ps < 4; ++ps) {
             if constexpr (kLrBatch) {
-                // u . l2^T of this pass's block rows from the staged rows on the
-                // 16x16x32 bf16 MFMA (u as hi + lo), interleaved over the
-                // column blocks so that consecutive MFMAs are independent
+                // Each block's accumulators leave the AGPRs once: converted,
+                // scaled and biased in one FMA into the f32 operand C of the
+                // 16x16x32 bf16 MFMA, which adds hi . l2^T and then
+                // lo . l2^T (u as hi + lo).  The VALU work of one block runs
+                // while the MFMAs of the block before it execute.
 #pragma unroll
                 for (int qb = 0; qb < kPassBlocks; ++qb) {
                     const int mb = ps * kPassBlocks + qb;
@@ -821,13 +813,14 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                         ul = *reinterpret_cast<const v8bf *>(ub + half_bytes + (urow * p.rp + j0) * 2);
                     }
 #pragma unroll
-                    for (int nb = 0; nb < kNBn; ++nb)
-                        set_blk(nb, mb, __builtin_bit_cast(blk_t, __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            al2[nb], uh, __builtin_bit_cast(v4f, blk(nb, mb)), 0, 0, 0)));
+                    for (int nb = 0; nb < kNBn; ++nb) {
+                        const blk_t c = blk(nb, mb);
+                        v4f t;
 #pragma unroll
-                    for (int nb = 0; nb < kNBn; ++nb)
-                        set_blk(nb, mb, __builtin_bit_cast(blk_t, __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            al2[nb], ul, __builtin_bit_cast(v4f, blk(nb, mb)), 0, 0, 0)));
+                        for (int e = 0; e < 4; ++e) t[e] = __builtin_fmaf((float)c[e], tm[mb], bias_at(nb, e));
+                        t = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al2[nb], uh, t, 0, 0, 0);
+                        lrv[qb][nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al2[nb], ul, t, 0, 0, 0);
+                    }
                 }
             }
 #pragma unroll
@@ -839,7 +832,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                     vals_t v;
                     const blk_t c = blk(nb, mb);
                     if constexpr (kLrBatch) {
-                        v = __builtin_bit_cast(vals_t, c);
+                        v = lrv[qb][nb];
                     } else {
 #pragma unroll
                         for (int e = 0; e < 4 * kQuads; ++e) {
@@ -875,7 +868,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                     for (int q = 0; q < kQuads; ++q) {
                         float y[4];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) y[i] = kFma ? v[4 * q + i] : v[4 * q + i] + bias_at(nb, 4 * q + i);
+                        for (int i = 0; i < 4; ++i)
+                            y[i] = kFma || kLrBatch ? v[4 * q + i] : v[4 * q + i] + bias_at(nb, 4 * q + i);
                         const float y0 = y[0], y1 = y[1], y2 = y[2], y3 = y[3];
                         const int row = qb * kBlk + brow;           // row within the pass
                         const int col = nb * kBlk + 8 * q + cq;     // bf16 column within the wave tile
