@@ -719,7 +719,47 @@ def _svd_prep_check(w_bits, r, iters, seed, sig_tol, lr_tol, energy_tol, what):
     # and its energy is close to the optimum (Eckart-Young)
     e_g, e_o = np.sum(got_v ** 2), np.sum(oracle.bf16_to_f64(res_o) ** 2)
     assert e_g <= e_o * (1.0 + energy_tol) + 1e-30, (what, e_g, e_o)
+    _svd_prep_apriori(w_bits, omega, r, iters, sg_g, p_g, what)
     return sg_g, sig_o
+
+
+def _svd_prep_apriori(w_bits, omega, r, iters, sg_g, p_g, what):
+    """The GPU preparation inside the windows that the subspace iteration's
+    theory fixes for this W and this test matrix (oracle.svd_prep.rsi_bounds:
+    singular values, spectral and Frobenius residual of the rank-r part),
+    widened by the precision of the GPU's arithmetic.  The sig_tol / lr_tol /
+    e_tol checks above are tighter regression guards set from measurement; these
+    windows are derived beforehand.
+
+    Precision terms: the singular values come from Zk = W^T Q, f32 sums of
+    2N exact products of bf16 W with Q stored as hi + lo bf16 halves (each
+    element within 2^-18 of Q); Higham's inner-product bound gives
+    |dZk| <= eps |W|^T |Q| with eps = 2^-18 + gamma_2N (1 + 2^-18),
+    gamma_n = n u / (1 - n u), u = 2^-24, and Weyl's inequality moves each
+    singular value by at most ||dZk||_F <= eps sqrt(s) ||W||_F (plus the f32
+    storage of sigma).  The rounding of the factors to bf16 (within 2^-9
+    elementwise) moves l2 . l1 by at most 2 2^-9 sqrt(sigma_1 sum sigma_j) +
+    2^-18 sum sigma_j in the spectral and the Frobenius norm.  The residuals
+    take the singular-value error delta to first order (the identity
+    ||W - A_r||_F^2 = ||W||_F^2 - sum_{j<=r} sigma^_j^2 of an orthonormal split)."""
+    from oracle import svd_prep
+    N, K = w_bits.shape
+    s = omega.shape[0]
+    b = svd_prep.rsi_bounds(w_bits, omega, r, iters)
+    w = oracle.bf16_to_f64(w_bits)
+    u = 2.0 ** -24
+    n2 = 2 * N
+    eps = 2.0 ** -18 + n2 * u / (1 - n2 * u) * (1 + 2.0 ** -18)
+    delta = eps * np.sqrt(s) * np.linalg.norm(w) + u * b["hi"][0] + 1e-30
+    assert np.all(sg_g >= b["lo"] - delta) and np.all(sg_g <= b["hi"] + delta), (what, "sigma window")
+    shi = b["hi"] + delta
+    rnd = 2 * 2.0 ** -9 * np.sqrt(shi[0] * shi.sum()) + 2.0 ** -18 * shi.sum()
+    e = w - p_g
+    gram = e.T @ e if e.shape[0] >= e.shape[1] else e @ e.T
+    spec_g = np.sqrt(max(np.linalg.eigvalsh(gram)[-1], 0.0))
+    assert spec_g <= b["spec"] + 2 * delta + rnd, (what, "spectral residual", spec_g, b["spec"])
+    fro_b = np.sum(w * w) - np.sum(np.maximum(b["lo"] - delta, 0.0) ** 2)
+    assert np.linalg.norm(e) <= np.sqrt(max(fro_b, 0.0)) + rnd, (what, "Frobenius residual")
 
 
 # Tolerances from the subspace-iteration error at this spectrum (sigma_i =

@@ -115,3 +115,69 @@ def test_low_rank_and_residual_definitions():
     assert np.array_equal(oracle.bf16_to_f64(w), p + e)          # W is exact in bf16
     assert np.array_equal(oracle.bf16_to_f64(svd_prep.residual(w, l2, l1)), e)
     assert not svd_prep.residual(oracle.f64_to_bf16(p), l2, l1).any()
+
+
+# ---------------------------------------------------------------------------
+# The subspace iteration of the oracle (svd_prep.rsi, the method the GPU
+# preparation computes) against the method's deterministic error bounds
+# (Halko, Martinsson and Tropp 2011, Theorems 9.1 and 9.2 and the construction
+# behind them), on planted spectra and a test matrix drawn as the GPU tests
+# draw it.  The bounds come from the exact SVD and the test matrix alone.
+
+def _omega(s, K, seed):
+    import workloads
+    return workloads.normal_bf16(np.random.default_rng(seed), (s, K), 1.0)
+
+
+def _planted_bits(seed, N, K, sigma):
+    w, _, _ = _planted(np.random.default_rng(seed), N, K, sigma)
+    return oracle.f64_to_bf16(w)
+
+
+SPECTRUM = 4.0 * 2.0 ** (-np.arange(128) / 4.0)
+
+
+@pytest.mark.parametrize("r,s,iters", [(16, 32, 2), (32, 48, 2), (8, 32, 0), (48, 64, 1), (64, 64, 2), (4, 16, 1)])
+def test_rsi_within_its_deterministic_bounds(r, s, iters):
+    wb = _planted_bits(r + 100 * iters, 512, 384, SPECTRUM)
+    om = _omega(s, 384, r + 7)
+    sg, u, vt = svd_prep.rsi(wb, om, r, iters)
+    b = svd_prep.rsi_bounds(wb, om, r, iters)
+    lo, hi, spec, fro, opt = b["lo"], b["hi"], b["spec"], b["fro"], b["opt"]
+    eps = 1e-12 * hi[0]
+    assert np.all(sg >= lo - eps) and np.all(sg <= hi + eps)
+    w = oracle.bf16_to_f64(wb)
+    a = (u * sg[None, :]) @ vt
+    assert np.linalg.norm(w - a, 2) <= spec + eps
+    e = float(np.sum((w - a) ** 2))
+    assert opt * (1 - 1e-12) - eps <= e <= fro * (1 + 1e-12) + eps   # Eckart-Young below, the bound above
+
+
+def test_rsi_bounds_are_tight_enough_to_see_a_dropped_power_iteration():
+    # the same test matrix without the two power iterations leaves the window
+    # of the iterated method (a mistake the bounds must catch)
+    wb = _planted_bits(232, 512, 384, SPECTRUM)
+    om = _omega(48, 384, 39)
+    b = svd_prep.rsi_bounds(wb, om, 32, 2)
+    lo, hi = b["lo"], b["hi"]
+    sg0, _, _ = svd_prep.rsi(wb, om, 32, 0)
+    assert np.any(sg0 < lo)
+    assert np.max(1 - lo / hi) < 1e-2
+
+
+def test_rsi_exact_when_the_subspace_holds_the_range():
+    # W = A B of rank 6 with small integer factors (entries exact in bf16),
+    # s = 16 >= 6: F = 0 at the split k = 6, the window closes and the
+    # iteration returns the exact SVD (no power iteration needed)
+    rng = np.random.default_rng(5)
+    w = rng.integers(-3, 4, (64, 6)).astype(np.float64) @ rng.integers(-3, 4, (6, 48)).astype(np.float64)
+    wb = oracle.f64_to_bf16(w)
+    assert np.array_equal(oracle.bf16_to_f64(wb), w) and np.linalg.matrix_rank(w) == 6
+    om = _omega(16, 48, 1)
+    b = svd_prep.rsi_bounds(wb, om, 6, 0)
+    lo, hi = b["lo"], b["hi"]
+    ref = np.linalg.svd(w, compute_uv=False)[:6]
+    assert np.allclose(lo, hi, rtol=1e-10) and np.allclose(hi, ref, rtol=1e-12)
+    sg, u, vt = svd_prep.rsi(wb, om, 6, 0)
+    assert np.allclose(sg, ref, rtol=1e-10)
+    assert np.linalg.norm(w - (u * sg[None, :]) @ vt) <= 1e-10 * np.linalg.norm(w)
