@@ -92,12 +92,20 @@ __global__ __launch_bounds__(kThreads) void svdq_down_kernel(const uint16_t *__r
 }
 
 // Fused launches (1) + (2) for K <= kFusedMaxK: one workgroup of kWaves waves
-// per 16 rows reads X once.  Each lane keeps its 16-byte chunks of the rows
-// (k steps wave, wave + kWaves, ...) in registers: their absmax meets in LDS
-// for the row scales, they feed the down-projection MFMAs, and they are
-// quantized with the act-quant kernel's arithmetic (same codes, same scales).
-constexpr int kFusedSteps = 8;  // k steps per wave held in registers
-constexpr int kFusedMaxK = kWaves * kFusedSteps * 32;
+// per 16 rows reads X once.  Wave w owns row m0 + w: it loads the row with
+// lane-interleaved 16-byte loads (each instruction reads 1 KB of the row),
+// takes the row absmax across the wave, writes the codes and the scale with
+// the act-quant kernel's arithmetic (same codes, same scales; 8 contiguous
+// code bytes per lane and chunk) and leaves the bf16 row in LDS.  The
+// down-projection u = X . L1^T then reads its bf16 MFMA fragments from LDS:
+// wave w takes the 32-wide k steps w, w + kWaves, ...; the l1 fragments of
+// those steps are requested from global memory before the row.
+constexpr int kFusedMaxK = 4096;
+constexpr int kFusedCpl = kFusedMaxK / 8 / 64;          // 16-byte chunks per lane and row
+constexpr int kFusedSteps = kFusedMaxK / 32 / kWaves;   // k steps per wave
+constexpr int kXsChunks = kFusedMaxK / 8;               // 16-byte chunks per staged row
+static_assert(kWaves == kRows, "one wave per row");
+static_assert(kWaves * kRows * (kMaxRp + 1) * 4 <= kRows * kXsChunks * 16, "partials fit in the row area");
 
 template <int QT, int JB>  // JB = rp / 16 column blocks of u
 __global__ __launch_bounds__(kThreads) void svdq_quant_down_kernel(const uint16_t *__restrict__ x, int M, int K,
@@ -105,90 +113,98 @@ __global__ __launch_bounds__(kThreads) void svdq_quant_down_kernel(const uint16_
                                                                    uint8_t *__restrict__ xq, float *__restrict__ sx,
                                                                    uint16_t *__restrict__ uhi,
                                                                    uint16_t *__restrict__ ulo) {
-    __shared__ float part[kWaves][kRows][kMaxRp + 1];
-    __shared__ uint32_t rmax[kWaves][kRows];
+    // The block's bf16 rows: chunk c of row i in slot c ^ i, so that the
+    // fragment reads of 16 rows at one chunk hit 16 distinct 16-byte bank
+    // groups, while each 1 KB row write stays one permuted contiguous KB.
+    // Once every wave's MFMAs are done, the same bytes hold the partial sums.
+    __shared__ __attribute__((aligned(16))) v4u xs[kRows][kXsChunks];
+    auto part = reinterpret_cast<float (*)[kRows][kMaxRp + 1]>(&xs[0][0]);
     constexpr float kQmax = QT == W8A8_INT8 ? 127.0f : 448.0f;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int m0 = blockIdx.x * kRows;
-    const int row = m0 + (lane & 15);
-    const int kq = (lane >> 4) * 8;  // this lane's 8 k values within a step
+    const int nchunks = K >> 3;  // K % 16 == 0: whole chunks
     const int nsteps = (K + 31) / 32;
+    const int fi = lane & 15, fg = lane >> 4;  // fragment row and 8-value k group of this lane
 
-    // K % 16 == 0: a chunk is either whole or past K
-    v4u d[kFusedSteps];
-#pragma unroll
-    for (int i = 0; i < kFusedSteps; ++i) {
-        const int k = (wave + i * kWaves) * 32 + kq;
-        d[i] = (row < M && k < K) ? *reinterpret_cast<const v4u *>(x + (size_t)row * K + k) : v4u{0u, 0u, 0u, 0u};
-    }
-    // l1 fragments of every step, all in flight at once: rows j >= r read
-    // zero (buffer range); where this lane's k is past K its x chunk is zero,
-    // so whatever l1 holds there adds nothing
+    // l1 fragments of this wave's steps, all in flight at once: rows j >= r
+    // read zero (buffer range); where a step's k is past K the staged row is
+    // zero, so whatever l1 holds there adds nothing
     const __amdgpu_buffer_rsrc_t rl1 =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(l1), (short)0, r * K * 2, kBufferRsrcWord3);
     v4u lf[kFusedSteps][JB];
 #pragma unroll
-    for (int i = 0; i < kFusedSteps; ++i) {
-        const int s = wave + i * kWaves;
+    for (int t = 0; t < kFusedSteps; ++t) {
+        const int s = wave + t * kWaves;
 #pragma unroll
         for (int b = 0; b < JB; ++b) {
-            const int j = b * 16 + (lane & 15);
-            lf[i][b] = s < nsteps ? __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(
-                                                                 rl1, (j * K + s * 32 + kq) * 2, 0, 0))
+            const int j = b * 16 + fi;
+            lf[t][b] = s < nsteps ? __builtin_bit_cast(v4u, __builtin_amdgcn_raw_buffer_load_b128(
+                                                                 rl1, (j * K + s * 32 + fg * 8) * 2, 0, 0))
                                   : v4u{0u, 0u, 0u, 0u};
         }
     }
+
+    // this wave's row: absmax, scale, codes; zeros past K and for rows past M
+    const int m = m0 + wave;
+    const v4u *xr = reinterpret_cast<const v4u *>(x + (size_t)(m < M ? m : 0) * K);
+    v4u d[kFusedCpl];
+#pragma unroll
+    for (int c = 0; c < kFusedCpl; ++c) {
+        const int chunk = c * 64 + lane;
+        d[c] = (m < M && chunk < nchunks) ? __builtin_nontemporal_load(xr + chunk) : v4u{0u, 0u, 0u, 0u};
+    }
     uint32_t m2 = 0;
 #pragma unroll
-    for (int i = 0; i < kFusedSteps; ++i) m2 = pk_max_u16(m2, chunk_absmax_bits(d[i]));
-    uint32_t mb = max(m2 & 0xFFFFu, m2 >> 16);  // bf16 magnitude bits; the 4 lanes of a row differ in bits 4, 5
-    mb = max(mb, (uint32_t)__shfl_xor((int)mb, 16, 64));
-    mb = max(mb, (uint32_t)__shfl_xor((int)mb, 32, 64));
-    if (lane < kRows) rmax[wave][lane] = mb;
+    for (int c = 0; c < kFusedCpl; ++c) m2 = pk_max_u16(m2, chunk_absmax_bits(d[c]));
+    const uint32_t mbits = wave_max_u32(max(m2 & 0xFFFFu, m2 >> 16));
+    if (m < M) {
+        const float sc = absmax_scale(bf16_bits_to_f32(mbits), kQmax);
+        const float rc = 1.0f / sc;
+        if (lane == 0) sx[m] = sc;
+        uint8_t *qrow = xq + (size_t)m * K;
+#pragma unroll
+        for (int c = 0; c < kFusedCpl; ++c) {
+            const int chunk = c * 64 + lane;
+            if (chunk < nchunks) *reinterpret_cast<uint2 *>(qrow + chunk * 8) = quantize8<QT>(d[c], sc, rc);
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < kFusedCpl; ++c) xs[wave][(c * 64 + lane) ^ wave] = d[c];
+    __syncthreads();
 
     v4f acc[JB];
 #pragma unroll
     for (int b = 0; b < JB; ++b) acc[b] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < kFusedSteps; ++i) {
-        if (wave + i * kWaves >= nsteps) break;
-        const v8bf_t a = __builtin_bit_cast(v8bf_t, d[i]);
+    for (int t = 0; t < kFusedSteps; ++t) {
+        const int s = wave + t * kWaves;
+        if (s >= nsteps) break;
+        const v8bf_t a = __builtin_bit_cast(v8bf_t, xs[fi][(s * 4 + fg) ^ fi]);
 #pragma unroll
         for (int b = 0; b < JB; ++b)
-            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf_t, lf[i][b]), acc[b], 0, 0, 0);
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(v8bf_t, lf[t][b]), acc[b], 0, 0, 0);
     }
+    __syncthreads();  // every wave has read its fragments before the partials overwrite the rows
+    // C layout of the 16x16 MFMA: lane l, element e -> row 4(l/16) + e, col l%16.
 #pragma unroll
     for (int b = 0; b < JB; ++b) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) part[wave][4 * (lane >> 4) + i][b * 16 + (lane & 15)] = acc[b][i];
+        for (int e = 0; e < 4; ++e) part[wave][4 * fg + e][b * 16 + fi] = acc[b][e];
     }
     __syncthreads();
-
-    // row scale and codes
-    uint32_t rm = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) rm = max(rm, rmax[w][lane & 15]);
-    const float sc = absmax_scale(bf16_bits_to_f32(rm), kQmax);
-    const float rc = 1.0f / sc;
-    if (wave == 0 && lane < kRows && row < M) sx[row] = sc;
-#pragma unroll
-    for (int i = 0; i < kFusedSteps; ++i) {
-        const int k = (wave + i * kWaves) * 32 + kq;
-        if (row < M && k < K) *reinterpret_cast<uint2 *>(xq + (size_t)row * K + k) = quantize8<QT>(d[i], sc, rc);
-    }
 
     // u = sum of the waves' partials, as hi + lo bf16 halves
     for (int idx = threadIdx.x; idx < kRows * rp; idx += kThreads) {
         const int rr = idx / rp, j = idx % rp;
-        const int m = m0 + rr;
-        if (m >= M) continue;
+        const int mm = m0 + rr;
+        if (mm >= M) continue;
         float u = part[0][rr][j];
 #pragma unroll
         for (int w = 1; w < kWaves; ++w) u += part[w][rr][j];
         const uint32_t hi = f32_to_bf16_bits(u);
         const uint32_t lo = f32_to_bf16_bits(u - bf16_bits_to_f32(hi));
-        uhi[(size_t)m * rp + j] = (uint16_t)hi;
-        ulo[(size_t)m * rp + j] = (uint16_t)lo;
+        uhi[(size_t)mm * rp + j] = (uint16_t)hi;
+        ulo[(size_t)mm * rp + j] = (uint16_t)lo;
     }
 }
 
