@@ -342,7 +342,6 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
 
     acc_t acc[kNBn][kNB];  // [weight block nb][activation block mb]
     auto blk = [&](int nb, int mb) -> blk_t { return acc[nb][mb]; };
-    auto set_blk = [&](int nb, int mb, blk_t c) { acc[nb][mb] = c; };
     frag_t fa[2][kNBn], fb[2][kNB];
 
     // int8: lane l reads row l & 15 of each 16-row block, 16-byte chunk
@@ -472,7 +471,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     // kt+2 .. kt+NST-2 whole, and the parts of stage kt+NST-1 issued so far
     constexpr int kPending = NST == 2 ? 0 : (NST - 3) * kLoads + (kParts - 1) * kPerPart;
     constexpr int kPendingDeferred = NST == 2 ? 0 : kPending - (kParts - 1) * kPerPart;
-    // Buffers of the low-rank operands: u (hi, then lo) in the tile's last
+    // e4m3 low-rank epilogue.  Buffers of the low-rank operands: u (hi, then lo) in the tile's last
     // stage's buffer, l2 in the buffer whose refill that stage defers (with
     // two stages the same 64 KB buffer, l2 after u's 32 KB).
     auto lr_ubuf = [&]() { return buf(std::integral_constant<int, NST - 1>{}); };
@@ -482,7 +481,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     };
     // buffer of the refill a tile's last stage defers (low-rank epilogue)
     constexpr int kDeferBuf = NST == 2 ? 1 : NST - 2;
-    // Low-rank epilogue (r of 16 or 32): the tile's low-rank operands go to
+    // e4m3 low-rank epilogue (r of 16 or 32): the tile's low-rank operands go to
     // the two ring buffers that the tile's last stage frees (its own, whose
     // fragments every wave read before the stage's barrier, and the one whose
     // refill it defers): u of the tile's 256 rows (hi, then lo, [256][rp]
@@ -518,13 +517,57 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                                                      0, 0);
         }
     };
-    // defer (the low-rank epilogue only, last stage of a tile): this stage's
-    // refill -- the next tile's stage NST - 2 -- is issued after the epilogue
-    // instead, so that its buffer can hold the low-rank operands meanwhile.
+    // int8 low-rank epilogue (kLrReg): no ring buffer is held across the
+    // epilogue, so every refill goes out on time.  l2 of the tile's 256
+    // columns comes by LDS-DMA into the second half of the waves' staging
+    // areas (wave w: tile columns 64w .. 64w + 63, [64][r] bf16) with the
+    // tile's other epilogue inputs, two stages before the epilogue; u comes
+    // from global memory into the fragment registers of the tile's last
+    // k-step, whose reads of the next stage's fragments would be dead (the
+    // next tile re-reads its stage 0 after the epilogue).
+    constexpr bool kLrReg = EPI == kEpiLowRank32 && kInt8;
+    constexpr int kLrL2Off = kOutWaveBytes / 2;
+    constexpr int kPLast = ((NST - 1) * KSTEPS + KSTEPS - 1) & 1;  // fragment set the tile's last k-step multiplies
+    static_assert(64 * kMaxRpStaged * 2 <= kOutWaveBytes - kLrL2Off, "l2 quarter fits the staging area's second half");
+    auto lowrank_l2_dma = [&](int n0) {  // n0: the tile's first column
+        const int cols_in = min(N - n0, 256);
+        const __amdgpu_buffer_rsrc_t rw2 = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(p.l2 + (size_t)n0 * p.r), (short)0, cols_in * p.r * 2, kBufferRsrcWord3);
+        uint8_t *dst = obuf + wave * kOutWaveBytes + kLrL2Off;
+        for (int i = 0; i < p.r / 8; ++i)  // 64 columns x r bf16 = 128 r bytes per wave, 1 KB per load
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rw2, (lds_ptr_t)(dst + i * 1024), 16,
+                                                     wave * 128 * p.r + i * 1024 + lane * 16, 0, 0, 0);
+    };
+    // u of the wave's 8 row blocks, hi into ah[mb] and lo into al[mb]: lane l
+    // holds row 16 mb + (l & 15), rank columns 8 (l >> 4) .. + 7 (zero past
+    // rp and for rows past M)
+    auto lowrank_u_loads = [&](frag_t *ah, frag_t *al) {
+      if constexpr (kLrReg) {
+        const int m0 = lr_mw - wm * 128;
+        const int rows_in = min(M - m0, 256);
+        const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(p.uhi + (size_t)m0 * p.rp), (short)0, rows_in * p.rp * 2, kBufferRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(p.ulo + (size_t)m0 * p.rp), (short)0, rows_in * p.rp * 2, kBufferRsrcWord3);
+        const int j0 = (lane >> 4) * 8;
+#pragma unroll
+        for (int mb = 0; mb < kNB; ++mb) {
+            const int off = j0 < p.rp ? ((wm * 128 + mb * 16 + (lane & 15)) * p.rp + j0) * 2 : kOobOffset;
+            ah[mb] = __builtin_bit_cast(frag_t, __builtin_amdgcn_raw_buffer_load_b128(rh, off, 0, 0));
+            al[mb] = __builtin_bit_cast(frag_t, __builtin_amdgcn_raw_buffer_load_b128(rl, off, 0, 0));
+        }
+      }
+    };
+    // defer (the low-rank epilogue only, last stage of a tile): for e4m3 this
+    // stage's refill -- the next tile's stage NST - 2 -- is issued after the
+    // epilogue instead, so that its buffer can hold the low-rank operands
+    // meanwhile; for int8 the stage's last k-step loads u into registers.
     auto run_stage = [&](auto sc, auto first_c, bool defer) {
         constexpr int S = decltype(sc)::value;
         constexpr bool FIRST = decltype(first_c)::value;
-        constexpr bool kMayDefer = EPI == kEpiLowRank32 && S == NST - 1;
+        constexpr bool kMayDefer = EPI == kEpiLowRank32 && !kInt8 && S == NST - 1;
+        // int8 low-rank, the tile's last stage (`defer` then marks it)
+        constexpr bool kLrRegLast = kLrReg && S == NST - 1;
         const bool issue = !kMayDefer || !defer;
         uint8_t *cur = buf(sc);
         uint8_t *nxt = buf(std::integral_constant<int, (S + 1) % NST>{});
@@ -547,6 +590,10 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                      __builtin_amdgcn_sched_barrier(0);
                      if constexpr (kMayDefer) {
                          if (defer) lowrank_dma();
+                         __builtin_amdgcn_sched_barrier(0);
+                     }
+                     if constexpr (kLrRegLast) {
+                         if (defer) lowrank_u_loads(fb[P ^ 1], fa[P ^ 1]);
                          __builtin_amdgcn_sched_barrier(0);
                      }
                  } else {
@@ -575,9 +622,11 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
                               for (int j = 0; j < 4; ++j)
                                   mfma_i8(acc[g / 2][(g % 2) * 4 + j], fa[P][g / 2], fb[P][(g % 2) * 4 + j], first);
                               [&]<int... R>(std::integer_sequence<int, R...>) {
-                                  (read_frag_i8(lp, std::integral_constant<int, spread_first(g, kReads, kGroups) + R>{},
-                                                fa[P ^ 1], fb[P ^ 1]),
-                                   ...);
+                                  // (the registers hold u on the int8 low-rank tile's last k-step)
+                                  if (!(kLrRegLast && kLast && defer))
+                                      (read_frag_i8(lp, std::integral_constant<int, spread_first(g, kReads, kGroups) + R>{},
+                                                    fa[P ^ 1], fb[P ^ 1]),
+                                       ...);
                               }(std::make_integer_sequence<int, spread_count(g, kReads, kGroups)>{});
                               [&]<int... L>(std::integer_sequence<int, L...>) {
                                   if (issue)
@@ -774,9 +823,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         uint8_t *ub = lr_ubuf();
         uint8_t *lb = lr_lbuf();
         const int half_bytes = 256 * p.rp * 2;
-        if constexpr (kLr32) {
-            // the tile's low-rank operands were issued at its last stage
-            // (lowrank_dma)
+        if constexpr (kLr32 && !kLrBatch) {
+            // e4m3: the tile's low-rank operands were issued at its last
+            // stage (lowrank_dma)
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             asm volatile("s_barrier" ::: "memory");
         }
@@ -784,12 +833,20 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
         // n of l2, the lane's 8 of up to 32 rank columns; zero past r)
         v8bf al2[kLrBatch ? kNBn : 1];
         if constexpr (kLrBatch) {
+            // from the second halves of the staging areas (lowrank_l2_dma,
+            // landed and made visible by the last stages' waits and barriers);
+            // every wave reads its l2 before any wave stages a pass there
             const int j0 = (el >> 4) * 8;
 #pragma unroll
             for (int nb = 0; nb < kNBn; ++nb) {
+                const int nl = wn * kWN + nb * 16 + brow;  // column within the tile
                 al2[nb] = v8bf{};
-                if (j0 < p.r) al2[nb] = *reinterpret_cast<const v8bf *>(lb + ((wn * kWN + nb * 16 + brow) * p.r + j0) * 2);
+                if (j0 < p.r)
+                    al2[nb] = *reinterpret_cast<const v8bf *>(obuf + (nl >> 6) * kOutWaveBytes + kLrL2Off +
+                                                             ((nl & 63) * p.r + j0) * 2);
             }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            asm volatile("s_barrier" ::: "memory");
         }
         // int8 low-rank: one pass's 16 blocks, dequantized with their bias
         // and then given u . l2^T
@@ -805,13 +862,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
 #pragma unroll
                 for (int qb = 0; qb < kPassBlocks; ++qb) {
                     const int mb = ps * kPassBlocks + qb;
-                    const int j0 = (el >> 4) * 8;
-                    const int urow = wm * 128 + mb * 16 + brow;
-                    v8bf uh = v8bf{}, ul = v8bf{};
-                    if (j0 < p.rp) {
-                        uh = *reinterpret_cast<const v8bf *>(ub + (urow * p.rp + j0) * 2);
-                        ul = *reinterpret_cast<const v8bf *>(ub + half_bytes + (urow * p.rp + j0) * 2);
-                    }
+                    const v8bf uh = __builtin_bit_cast(v8bf, fb[kPLast ^ 1][mb]);
+                    const v8bf ul = __builtin_bit_cast(v8bf, fa[kPLast ^ 1][mb]);
 #pragma unroll
                     for (int nb = 0; nb < kNBn; ++nb) {
                         const blk_t c = blk(nb, mb);
@@ -941,6 +993,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
             if constexpr (kDma) {
                 if (interior && kt0 + NST == kt_end) epi_dma(mw, nw);
             }
+            if constexpr (kLrReg) {
+                if (kt0 + NST == kt_end) lowrank_l2_dma(tc.n0);
+            }
             run_stages(std::integral_constant<int, NST - 2>{}, std::integral_constant<int, NST>{}, std::false_type{},
                        kt0 + NST == kt_end);
         }
@@ -948,6 +1003,15 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
             if (interior && kt_end == NST) {
                 epi_dma(mw, nw);
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+        }
+        if constexpr (kLrReg) {
+            // a tile of NST stages: its l2 goes out after them, and other
+            // waves read it
+            if (kt_end == NST) {
+                lowrank_l2_dma(tc.n0);
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                asm volatile("s_barrier" ::: "memory");
             }
         }
 
@@ -989,9 +1053,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
             if (interior) bf16_epilogue(std::true_type{}, mw, nw);
             else bf16_epilogue(std::false_type{}, mw, nw);
         }
-        // The staged u rows are read by every wave before any of them starts
-        // the next tile, whose first stage refills that buffer.
-        if constexpr (EPI == kEpiLowRank32) {
+        // e4m3: the staged u rows are read by every wave before any of them
+        // starts the next tile, whose first stage refills that buffer.
+        if constexpr (EPI == kEpiLowRank32 && !kInt8) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             asm volatile("s_barrier" ::: "memory");
             // the refill deferred from the tile's last stage (the next tile's
