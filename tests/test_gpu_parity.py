@@ -442,7 +442,10 @@ def test_int8_step_backward_sampled():
 # K > 4096 takes the two-kernel act-quant + down path; r = 24 rounds up to 32
 # but reads the factors from global memory in the epilogue
 @pytest.mark.parametrize("M,K,N,r", [(64, 256, 256, 32), (37, 96, 130, 5), (130, 512, 520, 16), (16, 64, 48, 64),
-                                     (40, 4160, 300, 32), (20, 8192, 64, 24), (33, 1024, 260, 24)])
+                                     (40, 4160, 300, 32), (20, 8192, 64, 24), (33, 1024, 260, 24),
+                                     # the fused kernel's largest K (every chunk and step of a wave used), its
+                                     # smallest (half a 32-wide step), and a K with a partial last step
+                                     (24, 4096, 200, 32), (17, 4096, 64, 16), (5, 16, 24, 16), (19, 48, 40, 32)])
 def test_svdq_small(qt, M, K, N, r):
     _say(f"svdq small qt={qt} M={M} K={K} N={N} r={r}")
     rng = np.random.default_rng(M + K + N + r)
