@@ -344,6 +344,12 @@ def main():
         del src, dst
 
     rows = {} if args.no_rows else other_rows(w8, torch, workloads, args)
+    svdq_row = rows.get("svdq_linear_M4096_K3072_N12288_r32")
+    if svdq_row:
+        # the SVDQuant linear against the plain step timed above (act-quant +
+        # product of the same shape): the low-rank branch's share of the time
+        svdq_row["plain_step_us"] = round(ms_step * 1e3, 1)
+        svdq_row["over_plain_step"] = round(svdq_row["us"] / (ms_step * 1e3) - 1.0, 4)
     for s in sets:
         s.clear()
     torch.cuda.empty_cache()
