@@ -522,9 +522,9 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     // columns comes by LDS-DMA into the second half of the waves' staging
     // areas (wave w: tile columns 64w .. 64w + 63, [64][r] bf16) with the
     // tile's other epilogue inputs, two stages before the epilogue; u comes
-    // from global memory into the fragment registers of the tile's last
-    // k-step, whose reads of the next stage's fragments would be dead (the
-    // next tile re-reads its stage 0 after the epilogue).
+    // from global memory, during the tile's last k-step, into the register
+    // set that k-step would fill with the next stage's fragments: those reads
+    // would be dead (the next tile re-reads its stage 0 after the epilogue).
     constexpr bool kLrReg = EPI == kEpiLowRank32 && kInt8;
     constexpr int kLrL2Off = kOutWaveBytes / 2;
     constexpr int kPLast = ((NST - 1) * KSTEPS + KSTEPS - 1) & 1;  // fragment set the tile's last k-step multiplies
@@ -542,21 +542,21 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmArgs p, int tiles_m,
     // holds row 16 mb + (l & 15), rank columns 8 (l >> 4) .. + 7 (zero past
     // rp and for rows past M)
     auto lowrank_u_loads = [&](frag_t *ah, frag_t *al) {
-      if constexpr (kLrReg) {
-        const int m0 = lr_mw - wm * 128;
-        const int rows_in = min(M - m0, 256);
-        const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(p.uhi + (size_t)m0 * p.rp), (short)0, rows_in * p.rp * 2, kBufferRsrcWord3);
-        const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(p.ulo + (size_t)m0 * p.rp), (short)0, rows_in * p.rp * 2, kBufferRsrcWord3);
-        const int j0 = (lane >> 4) * 8;
+        if constexpr (kLrReg) {
+            const int m0 = lr_mw - wm * 128;
+            const int rows_in = min(M - m0, 256);
+            const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(p.uhi + (size_t)m0 * p.rp), (short)0, rows_in * p.rp * 2, kBufferRsrcWord3);
+            const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(p.ulo + (size_t)m0 * p.rp), (short)0, rows_in * p.rp * 2, kBufferRsrcWord3);
+            const int j0 = (lane >> 4) * 8;
 #pragma unroll
-        for (int mb = 0; mb < kNB; ++mb) {
-            const int off = j0 < p.rp ? ((wm * 128 + mb * 16 + (lane & 15)) * p.rp + j0) * 2 : kOobOffset;
-            ah[mb] = __builtin_bit_cast(frag_t, __builtin_amdgcn_raw_buffer_load_b128(rh, off, 0, 0));
-            al[mb] = __builtin_bit_cast(frag_t, __builtin_amdgcn_raw_buffer_load_b128(rl, off, 0, 0));
+            for (int mb = 0; mb < kNB; ++mb) {
+                const int off = j0 < p.rp ? ((wm * 128 + mb * 16 + (lane & 15)) * p.rp + j0) * 2 : kOobOffset;
+                ah[mb] = __builtin_bit_cast(frag_t, __builtin_amdgcn_raw_buffer_load_b128(rh, off, 0, 0));
+                al[mb] = __builtin_bit_cast(frag_t, __builtin_amdgcn_raw_buffer_load_b128(rl, off, 0, 0));
+            }
         }
-      }
     };
     // defer (the low-rank epilogue only, last stage of a tile): for e4m3 this
     // stage's refill -- the next tile's stage NST - 2 -- is issued after the
