@@ -114,8 +114,11 @@ __device__ __forceinline__ uint32_t code_word(const float *v, float s, float r) 
 // same values (the staged-row kernel below dequantizes twice).  Steps past
 // the row's last block repeat that block (their writes rewrite the same
 // codes).  The codes are written over the staged blocks (all reads are done
-// by then) and the row leaves as 16-byte stores.
-template <int QT, int NSTEP>
+// by then) and the row leaves as 16-byte stores.  FULL: the row has exactly
+// 8 * NSTEP blocks, so no step is clamped and the lane's block of step q sits
+// at a fixed stride from its block of step 0: every step's LDS address is one
+// per-lane base plus an immediate offset (no address arithmetic per step).
+template <int QT, int NSTEP, bool FULL>
 __global__ __launch_bounds__(kThreads) void gguf_a8_requant_reg_kernel(const uint8_t *__restrict__ blocks,
                                                                        uint32_t total_bytes, int N, int K,
                                                                        int row_stage, uint8_t *__restrict__ wq,
@@ -133,11 +136,15 @@ __global__ __launch_bounds__(kThreads) void gguf_a8_requant_reg_kernel(const uin
 
     for (int n = blockIdx.x * (kThreads / 64) + wave; n < N; n += gridDim.x * (kThreads / 64)) {
         const int off = stage_row(rs, total_bytes, (uint32_t)n * row_bytes, row_bytes, st, lane);
+        const uint8_t *src0 = st + off + blk_in_step * 34;
+        uint8_t *dst0 = st + blk_in_step * 32 + 4 * part;
+        auto src = [&](int q) { return FULL ? src0 + q * (8 * 34) : st + off + min(8 * q + blk_in_step, nb - 1) * 34; };
+        auto dst = [&](int q) { return FULL ? dst0 + q * (8 * 32) : st + min(8 * q + blk_in_step, nb - 1) * 32 + 4 * part; };
         float v[NSTEP][4];
         float amax = 0.0f;
 #pragma unroll
         for (int q = 0; q < NSTEP; ++q) {
-            staged_block_vals<QT>(st + off + min(8 * q + blk_in_step, nb - 1) * 34, part, v[q]);
+            staged_block_vals<QT>(src(q), part, v[q]);
             amax = fmaxf(amax, fmaxf(fmaxf(fabsf(v[q][0]), fabsf(v[q][1])), fmaxf(fabsf(v[q][2]), fabsf(v[q][3]))));
         }
         // non-negative floats order like their bit patterns
@@ -145,9 +152,7 @@ __global__ __launch_bounds__(kThreads) void gguf_a8_requant_reg_kernel(const uin
         const float r = 1.0f / s;
         if (lane == 0) scale[n] = s;
 #pragma unroll
-        for (int q = 0; q < NSTEP; ++q)
-            *reinterpret_cast<uint32_t *>(st + min(8 * q + blk_in_step, nb - 1) * 32 + 4 * part) =
-                code_word<QT>(v[q], s, r);
+        for (int q = 0; q < NSTEP; ++q) *reinterpret_cast<uint32_t *>(dst(q)) = code_word<QT>(v[q], s, r);
         // the row's codes leave as 16-byte stores, 4 LDS reads per lane at a time
         uint8_t *orow = wq + (size_t)n * K;
         const int nout = K / 16;
@@ -377,9 +382,15 @@ extern "C" w8a8_status gguf_a8_requant_q8_0(w8a8_qtype qtype, const void *blocks
         const int64_t steps = (K / 32 + 7) / 8;  // 8-block steps per row
         const uint8_t *b8 = static_cast<const uint8_t *>(blocks);
         uint8_t *q8 = static_cast<uint8_t *>(wq);
-#define W8A8_GGUF_REG(QT, NS)                                                                                  \
-    gguf_a8_requant_reg_kernel<QT, NS><<<(int)grid, kThreads, lds, stream>>>(b8, (uint32_t)total, (int)N, (int)K, \
-                                                                            row_stage, q8, w_scale)
+#define W8A8_GGUF_REG(QT, NS)                                                                                   \
+    do {                                                                                                        \
+        if (K / 32 == 8 * (NS))                                                                                 \
+            gguf_a8_requant_reg_kernel<QT, NS, true><<<(int)grid, kThreads, lds, stream>>>(                     \
+                b8, (uint32_t)total, (int)N, (int)K, row_stage, q8, w_scale);                                   \
+        else                                                                                                    \
+            gguf_a8_requant_reg_kernel<QT, NS, false><<<(int)grid, kThreads, lds, stream>>>(                    \
+                b8, (uint32_t)total, (int)N, (int)K, row_stage, q8, w_scale);                                   \
+    } while (0)
         if (steps <= 16) {  // K <= 4096: register-resident rows
             if (qtype == W8A8_INT8) {
                 if (steps <= 4) W8A8_GGUF_REG(W8A8_INT8, 4);
