@@ -30,9 +30,14 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
-        build_oracle()
-    lib = ctypes.CDLL(LIB)
+    # W8A8_ORACLE_LIB: another build of w8a8_oracle.c (the mutation tests load
+    # deliberately broken copies through it to show that the pins catch them)
+    path = os.environ.get("W8A8_ORACLE_LIB")
+    if not path:
+        path = LIB
+        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+            build_oracle()
+    lib = ctypes.CDLL(path)
     P, I64, I, F, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_double
     sig = {
         "orc_bf16_to_f64": (D, [ctypes.c_uint16]),
