@@ -470,8 +470,10 @@ def test_svdq_small(qt, M, K, N, r):
 @pytest.mark.parametrize("K,r", [(256, 32), (1024, 16)])
 def test_svdq_multi_tile(qt, K, r):
     """More 256x256 tiles (17 x 17, ragged) than CUs, so workgroups run several
-    tiles back to back (the low-rank operands of one tile's epilogue share the
-    stage ring with the next tile's loads); K = 256 gives single-group tiles."""
+    tiles back to back (e4m3: the low-rank operands of one tile's epilogue
+    share the stage ring with the next tile's loads; int8: u arrives in the
+    registers of the tile's last k-step and l2 in the staging areas while the
+    next tile's stages load); K = 256 gives single-group tiles."""
     M, N = 4352 - 7, 4160 + 3
     _say(f"svdq multi-tile qt={qt} M={M} K={K} N={N} r={r}")
     rng = np.random.default_rng(K + r)
